@@ -1,0 +1,246 @@
+"""Plain fp64 paged attention over a block-table KV cache (CPU oracle).
+
+Test infrastructure only: imported by tests, the smoke check and the bench's
+CPU-baseline leg, never by the product path.  It shares no code with the HIP
+library and does not import it.
+
+What the pages fix and what is read into them
+---------------------------------------------
+The pages name paged attention over block tables and sequence lengths held as
+device tensors (vllm-metal architecture article, sections 三 and 四), prefix
+caching and chunked prefill (vllm-metis 0.1.0, intro and "How the model maps
+onto vLLM"), GQA 4:1 (vllm-metis 0.1.0, "Status") and FP8 with scale
+amax / 448 (same section).  They print no formula, layout or merge rule, so
+this oracle writes out the plain definition of each step:
+
+* attention of one query row:  out = softmax(scale * q . K^T) V over the
+  visible keys, scale = 1/sqrt(d) passed explicitly;
+* GQA: q-head j reads kv-head j // G, G = Hq / Hkv (contiguous groups);
+* decode: the query is the newest token, already in the cache, so it sees
+  keys 0 .. L-1 (L counts that token);
+* prefill chunk of n queries over a sequence of L tokens: context
+  ctx = L - n, query i sits at position ctx + i and sees keys 0 .. ctx + i
+  (causal, aligned to the bottom-right of the score matrix);
+* split-KV: partition p of size P covers tokens [pP, min((p+1)P, L)); it
+  yields its normalised output o_p and lse_p = ln sum exp(s); the merge is
+  out = sum_p w_p o_p / sum_p w_p with w_p = exp(lse_p - max lse);
+* FP8 KV: value = e4m3fn(code) * scale[kv_head], per K and per V.
+
+Layouts (see ``k_block`` / ``v_block``, the only two places that know them):
+k_cache[num_blocks, Hkv, block_size, d], v_cache[num_blocks, Hkv, d, block_size].
+Storage dtypes: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 codes.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import fp8_e4m3
+
+NEG_INF = -math.inf
+
+
+# ---------------------------------------------------------------------------
+# widening of stored values to float64 (exact for every storage type)
+# ---------------------------------------------------------------------------
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64.  bf16 bits are the top half of an fp32."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_e4m3.decode(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# the block-table walk
+# ---------------------------------------------------------------------------
+def k_block(k_cache, phys: int, h: int, n: int) -> np.ndarray:
+    """Keys of slots 0..n-1 of (physical block, kv-head): token-major K tile."""
+    return k_cache[phys, h, :n, :]
+
+
+def v_block(v_cache, phys: int, h: int, n: int) -> np.ndarray:
+    """Values of slots 0..n-1 of (physical block, kv-head), as rows [n, d]:
+    the V tile is stored dim-major, so its first n columns are read."""
+    return v_cache[phys, h, :, :n].T
+
+
+def gather_kv(k_cache, v_cache, table_row, seq_len: int, h: int, kv_dtype: str,
+              k_scale=None, v_scale=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Walk one sequence's block table, one logical block at a time, for kv-head h.
+
+    Logical token t lives in physical block table_row[t // bs] at slot t % bs.
+    Entries at or past ceil(L / bs) are never read, nor are slots past L in
+    the last block.  Returns float64 K [L, d] and V [L, d] (fp8 values
+    multiplied by the head's scale).
+    """
+    bs = k_cache.shape[2]
+    d = k_cache.shape[3]
+    K = np.empty((seq_len, d), dtype=np.float64)
+    V = np.empty((seq_len, d), dtype=np.float64)
+    for j in range(-(-seq_len // bs)):
+        phys = int(table_row[j])
+        n = min(bs, seq_len - j * bs)
+        K[j * bs:j * bs + n] = widen(k_block(k_cache, phys, h, n), kv_dtype)
+        V[j * bs:j * bs + n] = widen(v_block(v_cache, phys, h, n), kv_dtype)
+    if kv_dtype == "fp8":
+        K *= float(k_scale[h])
+        V *= float(v_scale[h])
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# attention of query rows against gathered keys
+# ---------------------------------------------------------------------------
+def attend(qrow: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> Tuple[np.ndarray, float]:
+    """softmax(scale * K q) V for one query row; returns (out[d], lse).
+
+    With no visible key the output is zeros and lse = -inf.
+    """
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64), NEG_INF
+    s = scale * (K @ qrow)
+    m = s.max()
+    e = np.exp(s - m)
+    den = e.sum()
+    return (e @ V) / den, float(m + math.log(den))
+
+
+def _heads(Hq: int, Hkv: int) -> int:
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return Hq // Hkv
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: str,
+           kv_dtype: str, k_scale=None, v_scale=None,
+           items: Optional[Iterable[Tuple[int, int]]] = None):
+    """Decode attention; returns (out[B, Hq, d], lse[B, Hq]) in float64.
+
+    ``items`` restricts the work to (sequence, kv-head) pairs; the other rows
+    are left NaN so that a caller cannot mistake them for results.
+    """
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = _heads(Hq, Hkv)
+    qf = widen(q, q_dtype)
+    out = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    todo = items if items is not None else [(b, h) for b in range(B) for h in range(Hkv)]
+    for b, h in todo:
+        K, V = gather_kv(k_cache, v_cache, block_table[b], int(seq_lens[b]), h, kv_dtype,
+                         k_scale, v_scale)
+        for g in range(G):
+            j = h * G + g
+            out[b, j], lse[b, j] = attend(qf[b, j], K, V, scale)
+    return out, lse
+
+
+def decode_partials(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: str,
+                    kv_dtype: str, partition_size: int, max_partitions: int,
+                    k_scale=None, v_scale=None):
+    """Per-partition (o_p, lse_p) of decode attention, float64.
+
+    Returns o [B, Hq, Pmax, d] and lse [B, Hq, Pmax]; partitions that hold no
+    token have o = 0 and lse = -inf.
+    """
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = _heads(Hq, Hkv)
+    P = partition_size
+    qf = widen(q, q_dtype)
+    o = np.zeros((B, Hq, max_partitions, d))
+    lse = np.full((B, Hq, max_partitions), NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(Hkv):
+            K, V = gather_kv(k_cache, v_cache, block_table[b], L, h, kv_dtype, k_scale, v_scale)
+            for p in range(-(-L // P)):
+                lo, hi = p * P, min((p + 1) * P, L)
+                for g in range(G):
+                    j = h * G + g
+                    o[b, j, p], lse[b, j, p] = attend(qf[b, j], K[lo:hi], V[lo:hi], scale)
+    return o, lse
+
+
+def merge(o_p: np.ndarray, lse_p: np.ndarray, seq_lens, partition_size: int):
+    """Log-sum-exp merge of partition results; returns (out[B,Hq,d], lse[B,Hq]).
+
+    Only partitions p < ceil(L / P) of a sequence take part; a sequence with
+    no partition gets zeros and lse = -inf.
+    """
+    B, Hq, _, d = o_p.shape
+    out = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        n = -(-int(seq_lens[b]) // partition_size)
+        if n == 0:
+            continue
+        for j in range(Hq):
+            ls = lse_p[b, j, :n]
+            M = ls.max()
+            if M == NEG_INF:
+                continue
+            w = np.exp(ls - M)
+            out[b, j] = (w[:, None] * o_p[b, j, :n]).sum(axis=0) / w.sum()
+            lse[b, j] = M + math.log(w.sum())
+    return out, lse
+
+
+def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: float,
+                  q_dtype: str, kv_dtype: str, k_scale=None, v_scale=None,
+                  items: Optional[Iterable[Tuple[int, int]]] = None):
+    """Causal chunked prefill; returns (out[total_q, Hq, d], lse[total_q, Hq]).
+
+    Chunk c holds queries cu[c] .. cu[c+1]-1 of a sequence of seq_lens[c]
+    tokens whose K/V (context and the chunk itself) are in the cache.  Query i
+    of the chunk sits at position ctx + i and attends to keys 0 .. ctx + i.
+    ``items`` restricts the work to (chunk, kv-head) pairs (others stay NaN).
+    """
+    total_q, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = _heads(Hq, Hkv)
+    qf = widen(q, q_dtype)
+    out = np.full((total_q, Hq, d), np.nan)
+    lse = np.full((total_q, Hq), np.nan)
+    n_chunks = len(seq_lens)
+    todo = items if items is not None else [(c, h) for c in range(n_chunks) for h in range(Hkv)]
+    for c, h in todo:
+        q0, q1 = int(cu_q_lens[c]), int(cu_q_lens[c + 1])
+        L = int(seq_lens[c])
+        ctx = L - (q1 - q0)
+        if ctx < 0:
+            raise ValueError("seq_len smaller than the chunk")
+        K, V = gather_kv(k_cache, v_cache, block_table[c], L, h, kv_dtype, k_scale, v_scale)
+        for i in range(q1 - q0):
+            visible = ctx + i + 1
+            for g in range(G):
+                j = h * G + g
+                out[q0 + i, j], lse[q0 + i, j] = attend(qf[q0 + i, j], K[:visible],
+                                                        V[:visible], scale)
+    return out, lse
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 results to the output storage type and widen back (for
+    comparing against values a kernel had to round): RNE to fp32, then to bf16."""
+    f = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    if dtype == "bf16":
+        bits = f.view(np.uint32).astype(np.uint64)
+        lsb = (bits >> np.uint64(16)) & np.uint64(1)
+        r = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+        return r.astype(np.uint32).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def items_for(seq_ids: Sequence[int], Hkv: int):
+    """All (sequence, kv-head) pairs of the given sequences."""
+    return [(int(b), h) for b in seq_ids for h in range(Hkv)]

@@ -1,0 +1,371 @@
+"""Seeded synthetic inputs for paged attention over a block-table KV cache.
+
+This module only draws and lays out inputs; it holds none of the attention
+arithmetic.  Both the HIP path (through the Python binding) and the CPU
+oracle consume exactly the arrays built here, so quantisation of the inputs
+never enters a parity error.
+
+Storage conventions (raw bits, so that each consumer widens them itself):
+
+* ``"f32"``  -> ``numpy.float32``
+* ``"bf16"`` -> ``numpy.uint16``  (bfloat16 bit patterns, round-to-nearest-even
+  from an fp32 draw, done by torch's CPU cast)
+* ``"fp8"``  -> ``numpy.uint8``   (OCP e4m3fn codes; one fp32 scale per kv-head)
+
+Cache layout (one contiguous tile per (block, kv-head)):
+
+* ``k_cache[num_blocks, num_kv_heads, block_size, head_dim]``  token-major
+* ``v_cache[num_blocks, num_kv_heads, head_dim, block_size]``  dim-major
+
+The pages name block tables and sequence lengths as the metadata of the paged
+cache and say the platform fixes the cache layout (vllm-metal architecture
+article, sections 二 and 四) but never give one; the layout above is this
+library's choice and is used identically by every consumer.
+
+Draw order per workload (one ``numpy.random.default_rng(seed)`` stream):
+sequence lengths -> pool permutation -> q -> K pool -> V pool.  K and V are
+drawn in fp32 N(0, 1) in chunks of 4096 blocks.  Sequence ``b`` takes the
+next ``ceil(L_b / block_size)`` entries of the permutation as its block-table
+row; unused table entries are padding (``-1`` by default).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BLOCK_SIZE = 16
+FP8_MAX = 448.0  # OCP e4m3fn largest finite value; scale rule amax / 448
+_CHUNK_BLOCKS = 4096
+
+__all__ = [
+    "DecodeWorkload", "PrefillWorkload", "MixedWorkload",
+    "config1", "config2", "config3", "config4", "config5", "build_config",
+    "decode_workload", "prefill_workload", "to_bf16_bits", "to_fp8_codes",
+    "kv_bytes_per_token", "CONFIG_NAMES",
+]
+
+CONFIG_NAMES = {
+    1: "tiny fp32 decode: 4 seqs, 8/2 heads, d=64, lens 1-200",
+    2: "Llama-3-8B-shaped layer decode bf16: 64 seqs, 32/8 heads, d=128, lens 512-4096",
+    3: "long-context split-KV decode bf16: 8 seqs, 32/8 heads, d=128, lens 32768-131072, partitions of 512",
+    4: "mixed chunked-prefill + prefix sharing bf16: 16 decode seqs (1024-8192) + 4 chunks of 512 over a 2048-token shared prefix",
+    5: "fp8-e4m3 KV decode: 256 seqs, 32/8 heads, d=128, lens 256-2048, per-kv-head scales",
+}
+
+
+# ---------------------------------------------------------------------------
+# dtype helpers (input preparation only)
+# ---------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> bfloat16 bit patterns (RNE), via torch's CPU cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def to_fp8_codes(x: np.ndarray, scale: np.ndarray, axis_scale: int) -> np.ndarray:
+    """Quantise fp32 ``x`` to e4m3fn codes with ``x / scale`` (true division).
+
+    ``scale`` is broadcast along ``axis_scale`` of ``x``.  Values are clamped to
+    +-448 before the cast (torch's cast does not saturate).
+    """
+    import torch
+    shape = [1] * x.ndim
+    shape[axis_scale] = -1
+    s = np.asarray(scale, dtype=np.float32).reshape(shape)
+    y = torch.from_numpy(np.ascontiguousarray(x / s, dtype=np.float32))
+    y = y.clamp_(-FP8_MAX, FP8_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def kv_bytes_per_token(num_kv_heads: int, head_dim: int, kv_bytes: float,
+                       num_layers: int = 1) -> float:
+    """K plus V bytes one token occupies: 2 * layers * kv-heads * d * bytes.
+
+    vllm-metis 0.1.0 ("How the model maps onto vLLM") prices its 6 KV layers
+    of 10 heads of 64 in BF16 at 15 KiB per token, which this formula gives.
+    """
+    return 2.0 * num_layers * num_kv_heads * head_dim * kv_bytes
+
+
+# ---------------------------------------------------------------------------
+# containers
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class DecodeWorkload:
+    """One decode query per sequence over a paged KV cache."""
+    name: str
+    q: np.ndarray                 # [B, Hq, d]   f32 / bf16 bits
+    k_cache: np.ndarray           # [NB, Hkv, bs, d]
+    v_cache: np.ndarray           # [NB, Hkv, d, bs]
+    block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
+    seq_lens: np.ndarray          # int32 [B]
+    q_dtype: str                  # "f32" | "bf16"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8"
+    scale: float                  # softmax scale, 1/sqrt(d)
+    k_scale: Optional[np.ndarray] = None   # f32 [Hkv] (fp8 only)
+    v_scale: Optional[np.ndarray] = None
+    partition_size: int = 0       # 0 = one pass per sequence
+
+    @property
+    def num_seqs(self) -> int: return int(self.q.shape[0])
+    @property
+    def num_q_heads(self) -> int: return int(self.q.shape[1])
+    @property
+    def head_dim(self) -> int: return int(self.q.shape[2])
+    @property
+    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
+    @property
+    def block_size(self) -> int: return int(self.k_cache.shape[2])
+    @property
+    def num_blocks(self) -> int: return int(self.k_cache.shape[0])
+    @property
+    def max_blocks_per_seq(self) -> int: return int(self.block_table.shape[1])
+    @property
+    def max_seq_len(self) -> int: return int(self.seq_lens.max()) if self.seq_lens.size else 0
+    @property
+    def total_tokens(self) -> int: return int(self.seq_lens.astype(np.int64).sum())
+
+    def kv_elem_bytes(self) -> int:
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes: live tokens only, all kv-heads."""
+        return int(self.total_tokens * kv_bytes_per_token(
+            self.num_kv_heads, self.head_dim, self.kv_elem_bytes()))
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """Causal prefill chunks over a paged context (bottom-right aligned)."""
+    name: str
+    q: np.ndarray                 # [total_q, Hq, d]
+    cu_q_lens: np.ndarray         # int32 [num_chunks + 1]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray       # int32 [num_chunks, max_blocks_per_seq]
+    seq_lens: np.ndarray          # int32 [num_chunks] = context + chunk length
+    q_dtype: str
+    kv_dtype: str
+    scale: float
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+
+    @property
+    def num_chunks(self) -> int: return int(self.seq_lens.shape[0])
+    @property
+    def total_q(self) -> int: return int(self.q.shape[0])
+    @property
+    def num_q_heads(self) -> int: return int(self.q.shape[1])
+    @property
+    def head_dim(self) -> int: return int(self.q.shape[2])
+    @property
+    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
+    @property
+    def block_size(self) -> int: return int(self.k_cache.shape[2])
+    @property
+    def num_blocks(self) -> int: return int(self.k_cache.shape[0])
+    @property
+    def max_blocks_per_seq(self) -> int: return int(self.block_table.shape[1])
+    @property
+    def q_lens(self) -> np.ndarray: return np.diff(self.cu_q_lens).astype(np.int64)
+    @property
+    def max_q_len(self) -> int: return int(self.q_lens.max()) if self.num_chunks else 0
+
+    def pairs(self) -> int:
+        """Visible (query, key) pairs per head: sum over queries of ctx + i + 1."""
+        total = 0
+        for c in range(self.num_chunks):
+            n = int(self.q_lens[c]); ctx = int(self.seq_lens[c]) - n
+            total += n * ctx + n * (n + 1) // 2
+        return total
+
+    def flops(self) -> float:
+        """QK^T and PV multiply-adds at 2 flops each, all q-heads."""
+        return 4.0 * self.pairs() * self.num_q_heads * self.head_dim
+
+
+@dataclasses.dataclass
+class MixedWorkload:
+    """Decode rows and prefill chunks sharing one physical pool."""
+    name: str
+    decode: DecodeWorkload
+    prefill: PrefillWorkload
+
+
+# ---------------------------------------------------------------------------
+# drawing
+# ---------------------------------------------------------------------------
+def _draw_pool(rng, num_blocks, num_kv_heads, head_dim, block_size, dtype):
+    """Draw one N(0,1) pool of num_blocks tiles in chunks; returns storage array
+    (f32 or bf16 bits) or, for fp8, the fp32 pool (quantised later)."""
+    tile = num_kv_heads * head_dim * block_size
+    if dtype == "bf16":
+        out = np.empty(num_blocks * tile, dtype=np.uint16)
+    else:
+        out = np.empty(num_blocks * tile, dtype=np.float32)
+    for b0 in range(0, num_blocks, _CHUNK_BLOCKS):
+        b1 = min(num_blocks, b0 + _CHUNK_BLOCKS)
+        x = rng.standard_normal((b1 - b0) * tile, dtype=np.float32)
+        out[b0 * tile:b1 * tile] = to_bf16_bits(x) if dtype == "bf16" else x
+    return out
+
+
+def _quantise_pool_fp8(pool_f32, num_kv_heads):
+    """Per-kv-head amax/448 scale, then e4m3fn codes.  pool: [NB, Hkv, ...]."""
+    nb = pool_f32.shape[0]
+    amax = np.abs(pool_f32.reshape(nb, num_kv_heads, -1)).max(axis=(0, 2))
+    scale = (amax.astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
+    codes = to_fp8_codes(pool_f32, scale, axis_scale=1)
+    return codes, scale
+
+
+def _tables_from_perm(perm, lens, block_size, max_blocks, pad):
+    table = np.full((len(lens), max_blocks), pad, dtype=np.int32)
+    pos = 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // block_size)
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    return table, pos
+
+
+def _make_pools(rng, nb, hkv, d, bs, kv_dtype):
+    k = _draw_pool(rng, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
+    v = _draw_pool(rng, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
+    k = k.reshape(nb, hkv, bs, d)
+    v = v.reshape(nb, hkv, d, bs)
+    ks = vs = None
+    if kv_dtype == "fp8":
+        k, ks = _quantise_pool_fp8(k, hkv)
+        v, vs = _quantise_pool_fp8(v, hkv)
+    return k, v, ks, vs
+
+
+def _draw_q(rng, shape, q_dtype):
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    return to_bf16_bits(x) if q_dtype == "bf16" else x
+
+
+def decode_workload(*, seed: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                    head_dim: int, len_lo: int, len_hi: int, q_dtype: str, kv_dtype: str,
+                    block_size: int = BLOCK_SIZE, pool_blocks: Optional[int] = None,
+                    partition_size: int = 0, pad: int = -1, seq_lens=None,
+                    name: str = "decode") -> DecodeWorkload:
+    """Generic seeded decode workload (lengths uniform integers in [lo, hi])."""
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        lens = rng.integers(len_lo, len_hi, size=num_seqs, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    need = int(sum(-(-int(L) // block_size) for L in lens))
+    nb = max(need, 1) if pool_blocks is None else int(pool_blocks)
+    if nb < need:
+        raise ValueError("pool too small for the drawn lengths")
+    perm = rng.permutation(nb).astype(np.int32)
+    max_blocks = max(1, -(-int(lens.max(initial=0)) // block_size))
+    table, _ = _tables_from_perm(perm, lens, block_size, max_blocks, pad)
+    q = _draw_q(rng, (num_seqs, num_q_heads, head_dim), q_dtype)
+    k, v, ks, vs = _make_pools(rng, nb, num_kv_heads, head_dim, block_size, kv_dtype)
+    return DecodeWorkload(name=name, q=q, k_cache=k, v_cache=v, block_table=table,
+                          seq_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                          scale=1.0 / math.sqrt(head_dim), k_scale=ks, v_scale=vs,
+                          partition_size=partition_size)
+
+
+def prefill_workload(*, seed: int, q_lens, ctx_lens, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, q_dtype: str, kv_dtype: str, block_size: int = BLOCK_SIZE,
+                     pad: int = -1, name: str = "prefill") -> PrefillWorkload:
+    """Generic seeded prefill-chunk workload with private blocks per chunk."""
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    lens = (np.asarray(ctx_lens, dtype=np.int32) + q_lens).astype(np.int32)
+    need = int(sum(-(-int(L) // block_size) for L in lens))
+    nb = max(need, 1)
+    perm = rng.permutation(nb).astype(np.int32)
+    max_blocks = max(1, -(-int(lens.max(initial=0)) // block_size))
+    table, _ = _tables_from_perm(perm, lens, block_size, max_blocks, pad)
+    cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    q = _draw_q(rng, (int(cu[-1]), num_q_heads, head_dim), q_dtype)
+    k, v, ks, vs = _make_pools(rng, nb, num_kv_heads, head_dim, block_size, kv_dtype)
+    return PrefillWorkload(name=name, q=q, cu_q_lens=cu, k_cache=k, v_cache=v,
+                           block_table=table, seq_lens=lens, q_dtype=q_dtype,
+                           kv_dtype=kv_dtype, scale=1.0 / math.sqrt(head_dim),
+                           k_scale=ks, v_scale=vs)
+
+
+# ---------------------------------------------------------------------------
+# the five configurations
+# ---------------------------------------------------------------------------
+def config1(pad: int = -1) -> DecodeWorkload:
+    """Tiny fp32: 4 seqs, 8/2 heads (GQA 4), d=64, lens U{1..200}, pool of 64."""
+    return decode_workload(seed=1, num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                           len_lo=1, len_hi=200, q_dtype="f32", kv_dtype="f32",
+                           pool_blocks=64, pad=pad, name="C1")
+
+
+def config2(pad: int = -1, partition_size: int = 512) -> DecodeWorkload:
+    """Llama-3-8B layer decode, bf16: 64 seqs, 32/8 heads, d=128, lens U{512..4096}."""
+    return decode_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=512, len_hi=4096, q_dtype="bf16", kv_dtype="bf16",
+                           pad=pad, partition_size=partition_size, name="C2")
+
+
+def config3(pad: int = -1) -> DecodeWorkload:
+    """Long-context split-KV, bf16: 8 seqs, lens U{32768..131072}, partitions of 512."""
+    return decode_workload(seed=3, num_seqs=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=32768, len_hi=131072, q_dtype="bf16", kv_dtype="bf16",
+                           pad=pad, partition_size=512, name="C3")
+
+
+def config4(pad: int = -1, partition_size: int = 512) -> MixedWorkload:
+    """Mixed step: 16 decode seqs (U{1024..8192}) + 4 prefill chunks of 512 new tokens
+    over a 2048-token prefix whose 128 blocks every chunk table references.
+
+    Pool order: prefix blocks, then each chunk's 32 private blocks, then the
+    decode sequences' blocks, all taken from one permutation.
+    """
+    bs, hq, hkv, d = BLOCK_SIZE, 32, 8, 128
+    rng = np.random.default_rng(4)
+    dec_lens = rng.integers(1024, 8192, size=16, endpoint=True).astype(np.int32)
+    n_chunks, q_len, ctx = 4, 512, 2048
+    prefix_blocks, private_blocks = ctx // bs, q_len // bs
+    dec_blocks = int(sum(-(-int(L) // bs) for L in dec_lens))
+    nb = prefix_blocks + n_chunks * private_blocks + dec_blocks
+    perm = rng.permutation(nb).astype(np.int32)
+    pos = 0
+    prefix = perm[pos:pos + prefix_blocks]; pos += prefix_blocks
+    ptab = np.full((n_chunks, prefix_blocks + private_blocks), pad, dtype=np.int32)
+    for c in range(n_chunks):
+        ptab[c, :prefix_blocks] = prefix
+        ptab[c, prefix_blocks:] = perm[pos:pos + private_blocks]; pos += private_blocks
+    dtab, _ = _tables_from_perm(perm[pos:], dec_lens, bs,
+                                -(-int(dec_lens.max()) // bs), pad)
+    q_dec = _draw_q(rng, (16, hq, d), "bf16")
+    q_pre = _draw_q(rng, (n_chunks * q_len, hq, d), "bf16")
+    k, v, _, _ = _make_pools(rng, nb, hkv, d, bs, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    dec = DecodeWorkload(name="C4-decode", q=q_dec, k_cache=k, v_cache=v, block_table=dtab,
+                         seq_lens=dec_lens, q_dtype="bf16", kv_dtype="bf16", scale=scale,
+                         partition_size=partition_size)
+    cu = np.arange(n_chunks + 1, dtype=np.int32) * q_len
+    pre = PrefillWorkload(name="C4-prefill", q=q_pre, cu_q_lens=cu, k_cache=k, v_cache=v,
+                          block_table=ptab, seq_lens=np.full(n_chunks, ctx + q_len, np.int32),
+                          q_dtype="bf16", kv_dtype="bf16", scale=scale)
+    return MixedWorkload(name="C4", decode=dec, prefill=pre)
+
+
+def config5(pad: int = -1, partition_size: int = 512) -> DecodeWorkload:
+    """fp8-e4m3 KV decode: 256 seqs, lens U{256..2048}, per-kv-head amax/448 scales,
+    q and output bf16."""
+    return decode_workload(seed=5, num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=256, len_hi=2048, q_dtype="bf16", kv_dtype="fp8",
+                           pad=pad, partition_size=partition_size, name="C5")
+
+
+def build_config(n: int, **kw):
+    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)
