@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+Headline: KV GB/s (and % of the 8 TB/s HBM peak) plus tokens-attended/s of
+bf16 decode at the Llama-3-8B layer shape: 64 sequences, 32 q-heads / 8
+kv-heads, head_dim 128, block_size 16, lengths uniform in [512, 4096] (seed
+2), block tables a random permutation of one pool.  A step is one pass of
+the decode path over that batch: the split-KV partition kernel plus the
+log-sum-exp merge (pa_decode's two launches), inputs resident in HBM.  Before
+every timed step a 1 GiB buffer is rewritten so no KV survives in the 256 MB
+Infinity Cache; step times come from HIP events on the launch stream.
+
+The other workloads (long-context split-KV, the mixed chunked-prefill step,
+fp8 KV) are timed the same way and reported under "per_config".  The
+CPU-baseline leg times the fp64 oracle on the host over the whole headline
+batch (single thread).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode KV GB/s (% HBM peak) + tokens-attended/s, Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+FLUSH_BYTES = 1 << 30
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands, single-threaded, over the whole batch."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                      wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
+        dt = time.perf_counter() - t0
+    return {"value": round(wl.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "tokens_attended_per_s": round(wl.total_tokens / dt, 1),
+            "sample": f"whole batch: {wl.num_seqs} sequences, {wl.total_tokens} tokens, "
+                      f"all {wl.num_kv_heads} kv-heads (fp64 numpy oracle, 1 thread)"}
+
+
+class Timer:
+    """Per-step HIP events on the current stream, around each launch group."""
+
+    def __init__(self, torch, n, marks):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(n)]
+
+    def ms(self, i, a, b):
+        return self.ev[i][a].elapsed_time(self.ev[i][b])
+
+
+def time_decode(torch, pa, d, wl, P, steps, warmup, flush):
+    """Returns (per-step ms list, per-step partition-kernel ms list)."""
+    B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
+    out = torch.empty_like(d.q)
+    if P > 0:
+        pmax = -(-wl.max_seq_len // P)
+        po = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device="cuda")
+        pl = torch.empty((B, Hq, pmax), dtype=torch.float32, device="cuda")
+
+    def launch(ev):
+        ev[0].record()
+        if P > 0:
+            pa.decode_partitions(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                                 partition_size=P, scale=wl.scale, k_scale=d.ks, v_scale=d.vs,
+                                 partial_out=po, partial_lse=pl)
+            ev[1].record()
+            pa.merge_partitions(po, pl, d.sl, partition_size=P, out=out)
+        else:
+            pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                      partition_size=0, k_scale=d.ks, v_scale=d.vs, out=out)
+            ev[1].record()
+        ev[2].record()
+
+    wt = Timer(torch, warmup, 3)
+    for i in range(warmup):
+        flush.add_(1)
+        launch(wt.ev[i])
+    torch.cuda.synchronize()
+    t = Timer(torch, steps, 3)
+    for i in range(steps):
+        flush.add_(1)
+        launch(t.ev[i])
+    torch.cuda.synchronize()
+    return [t.ms(i, 0, 2) for i in range(steps)], [t.ms(i, 0, 1) for i in range(steps)]
+
+
+def time_prefill(torch, pa, d, wl, steps, warmup, flush):
+    out = torch.empty_like(d.q)
+
+    def launch(ev):
+        ev[0].record()
+        pa.prefill_chunk(d.q, d.cu, d.k, d.v, d.bt, d.sl, max_q_len=wl.max_q_len, scale=wl.scale,
+                         out=out)
+        ev[1].record()
+
+    wt = Timer(torch, warmup, 2)
+    for i in range(warmup):
+        flush.add_(1)
+        launch(wt.ev[i])
+    torch.cuda.synchronize()
+    t = Timer(torch, steps, 2)
+    for i in range(steps):
+        flush.add_(1)
+        launch(t.ev[i])
+    torch.cuda.synchronize()
+    return [t.ms(i, 0, 1) for i in range(steps)]
+
+
+def med(xs):
+    s = sorted(xs)
+    return s[len(s) // 2]
+
+
+def decode_summary(wl, step_ms, kern_ms):
+    kv = wl.kv_bytes()
+    ms = sum(step_ms) / len(step_ms)
+    kms = sum(kern_ms) / len(kern_ms)
+    return {
+        "ms_per_step": round(ms, 5), "kv_GBps": round(kv / ms / 1e6, 2),
+        "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
+        "tokens_attended_per_s": round(wl.total_tokens / ms * 1e3, 1),
+        "partition_kernel_ms": round(kms, 5),
+        "partition_kernel_GBps": round(kv / kms / 1e6, 2),
+        "p10_ms": round(sorted(step_ms)[len(step_ms) // 10], 5),
+        "p50_ms": round(med(step_ms), 5),
+        "p90_ms": round(sorted(step_ms)[(9 * len(step_ms)) // 10], 5),
+        "kv_bytes": kv, "total_tokens": wl.total_tokens,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the kernels run on one GPU's share; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import workloads as W
+    wl = W.config2(pad=0, partition_size=args.partition_size)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)   # before any GPU use
+
+    import torch
+    import paged_kv_cache_22_amd as pa
+    from workloads.device import Dev
+
+    torch.cuda.init()
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    d = Dev(wl)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms, kern_ms = time_decode(torch, pa, d, wl, args.partition_size, args.steps,
+                                   args.warmup, flush)
+    wall = time.perf_counter() - t0
+    head = decode_summary(wl, step_ms, kern_ms)
+    del d
+
+    per_config = {}
+    if not args.headline_only:
+        for n, P in ((3, 512), (5, args.partition_size)):
+            w = W.build_config(n, pad=0) if n == 3 else W.build_config(n, pad=0, partition_size=P)
+            dd = Dev(w)
+            s, k = time_decode(torch, pa, dd, w, w.partition_size, 20, 3, flush)
+            per_config[w.name] = decode_summary(w, s, k)
+            per_config[w.name]["workload"] = W.CONFIG_NAMES[n]
+            del dd
+        m = W.config4(pad=0, partition_size=args.partition_size)
+        dd, dp = Dev(m.decode), Dev(m.prefill)
+        s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, 20, 3, flush)
+        pms = time_prefill(torch, pa, dp, m.prefill, 20, 3, flush)
+        pre_ms = sum(pms) / len(pms)
+        dec = decode_summary(m.decode, s, k)
+        tflops = m.prefill.flops() / pre_ms / 1e9
+        per_config["C4"] = {
+            "workload": W.CONFIG_NAMES[4],
+            "step_ms": round(dec["ms_per_step"] + pre_ms, 5),
+            "decode": dec,
+            "prefill": {"ms": round(pre_ms, 5), "TFLOPs": round(tflops, 2),
+                        "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+                        "pairs": m.prefill.pairs(), "flops": m.prefill.flops(),
+                        "tokens_attended_per_s": round(m.prefill.pairs() / pre_ms * 1e3, 1)},
+        }
+
+    kv = head["kv_GBps"]
+    line = {
+        "metric": METRIC,
+        "value": kv,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3-8B-shaped layer decode, bf16: 64 seqs, 32 q-heads / 8 "
+                               "kv-heads, head_dim 128, block_size 16, lens U[512,4096] seed 2, "
+                               "block tables a random permutation of one pool",
+                   "global_batch": wl.num_seqs, "seq_len": "512-4096",
+                   "total_tokens": wl.total_tokens, "partition_size": args.partition_size,
+                   "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "tokens_attended_per_s": head["tokens_attended_per_s"],
+        "timing": {"p10_ms": head["p10_ms"], "p50_ms": head["p50_ms"], "p90_ms": head["p90_ms"],
+                   "wall_s_incl_cache_flush": round(wall, 3),
+                   "note": "per-step HIP events around the launches; a 1 GiB rewrite before "
+                           "each step evicts the Infinity Cache and is not timed"},
+        "roofline": {
+            "kernel": "decode_kernel<128, bf16, split>",
+            "bound": "hbm",
+            "achieved": head["partition_kernel_GBps"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["partition_kernel_GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": head["kv_bytes"],
+            "avg_launch_ms": head["partition_kernel_ms"],
+        },
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * pa.h -- paged attention over a block-table KV cache, for AMD Instinct
+ * MI355X (gfx950).  C ABI of libpa.so.
+ *
+ * What is computed.  The pages this library follows name the pieces but not
+ * the formulas: paged attention whose block table and sequence lengths stay
+ * device tensors handed to the kernels (vllm-metal architecture article,
+ * sections 三 and 四), prefix caching and chunked prefill (vllm-metis 0.1.0,
+ * intro and "How the model maps onto vLLM"), GQA 4:1 (vllm-metis 0.1.0,
+ * "Status") and FP8 with one scale of amax / 448 (same section).  Each call
+ * below computes, for every query row, the plain definition
+ *
+ *     out = softmax(scale * q . K^T) V
+ *
+ * over the keys the row may see, with q-head j reading kv-head j / G
+ * (G = num_q_heads / num_kv_heads, contiguous groups).
+ *
+ * Memory layouts (row-major, contiguous, all device memory):
+ *   q, out (decode)    [num_seqs, num_q_heads, head_dim]
+ *   q, out (prefill)   [total_q,  num_q_heads, head_dim]
+ *   k_cache            [num_blocks, num_kv_heads, block_size, head_dim]  (token-major tiles)
+ *   v_cache            [num_blocks, num_kv_heads, head_dim, block_size]  (dim-major tiles)
+ *   block_table        int32 [num_seqs, max_blocks_per_seq]; logical token t of
+ *                      sequence b lives in physical block block_table[b][t / block_size]
+ *                      at slot t % block_size
+ *   seq_lens           int32 [num_seqs]; tokens whose K/V are in the cache,
+ *                      including the current decode token or the whole chunk
+ *   k_scale, v_scale   fp32 [num_kv_heads] (fp8 KV only; NULL otherwise):
+ *                      K value = e4m3fn(code) * k_scale[kv_head], likewise V
+ *   partial_out        fp32 [num_seqs, num_q_heads, max_partitions, head_dim]
+ *   partial_lse        fp32 [num_seqs, num_q_heads, max_partitions], natural log
+ *
+ * Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ * num_kv_heads with G <= 16; dtypes (q, kv) = (F32, F32), (BF16, BF16) or
+ * (BF16, FP8_E4M3); out has q's dtype; q, out, k_cache, v_cache 16-byte
+ * aligned.
+ *
+ * Ownership and execution.  The library owns no memory and keeps no state
+ * between calls.  Every call only validates its scalar arguments and pointer
+ * alignment on the host and enqueues kernels on `stream` (a hipStream_t;
+ * NULL = the default stream).  It never reads device memory from the host,
+ * never synchronises and never allocates, so calls can be captured in a HIP
+ * graph.  Table entries at or past ceil(seq_len / block_size) and cache
+ * slots past seq_len are never read (they may hold anything, NaN included).
+ *
+ * Errors.  A non-zero pa_status is returned before anything is enqueued when
+ * the arguments are invalid.  PA_ERR_HIP reports a failed launch (including a
+ * library built without a gfx950 code object).  There is no fallback path.
+ * Block-table contents are not checked: an entry outside [0, num_blocks) or
+ * a seq_len above max_blocks_per_seq * block_size is undefined behaviour.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_F32 = 0,
+    PA_BF16 = 1,
+    PA_FP8_E4M3 = 2   /* OCP e4m3fn (largest finite 448), KV cache only */
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,         /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,        /* a size is negative, inconsistent or too large */
+    PA_ERR_DTYPE = 3,        /* unknown dtype or unsupported (q, kv) pair */
+    PA_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
+    PA_ERR_UNSUPPORTED = 5,  /* head_dim, block_size, G or partition size not supported */
+    PA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required */
+    PA_ERR_HIP = 7           /* the HIP runtime rejected a launch */
+} pa_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+/*
+ * Bytes of workspace pa_decode needs: 0 when partition_size == 0, else room
+ * for fp32 partials [num_seqs, num_q_heads, P_max, head_dim] and their lse
+ * [num_seqs, num_q_heads, P_max], P_max = ceil(max_seq_len / partition_size),
+ * each region 256-byte aligned.  Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                int max_seq_len, int partition_size);
+
+/*
+ * Decode attention: one query per sequence (the newest token, already in the
+ * cache) attends to keys 0 .. seq_lens[b]-1.
+ *
+ * partition_size == 0: one pass per (sequence, kv-head), out written
+ * directly.  partition_size > 0 (a multiple of block_size): split-KV; each
+ * partition p covers tokens [p*P, min((p+1)*P, L)) and writes its normalised
+ * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
+ * pa_merge_partitions) writes out.  max_seq_len is the caller's host-side
+ * bound on seq_lens; it sizes the grid.  A sequence of length 0 gets zeros.
+ * scale is the softmax scale (1/sqrt(head_dim) for plain attention); it
+ * must be finite and > 0 (PA_ERR_SHAPE otherwise), and so must every fp8
+ * k_scale / v_scale entry (not checked: device data).
+ */
+int pa_decode(void* out, const void* q, int q_dtype,
+              const void* k_cache, const void* v_cache, int kv_dtype,
+              const int32_t* block_table, int max_blocks_per_seq,
+              const int32_t* seq_lens, int num_seqs,
+              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, float scale, const float* k_scale, const float* v_scale,
+              int partition_size, int max_seq_len,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split-KV decode, partition kernel only: writes partial_out / partial_lse
+ * for every partition of every sequence (partitions past ceil(L / P) are not
+ * written and must not be read; pa_merge_partitions ignores them).
+ * max_partitions is the P_max dimension of the partial arrays and must be at
+ * least ceil(max_seq_len / partition_size).  partition_size > 0.
+ */
+int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partitions,
+                         const void* q, int q_dtype,
+                         const void* k_cache, const void* v_cache, int kv_dtype,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int num_seqs,
+                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, float scale, const float* k_scale,
+                         const float* v_scale, int partition_size, int max_seq_len,
+                         void* stream);
+
+/*
+ * Log-sum-exp merge of split-KV partials.  For sequence b only partitions
+ * p < ceil(seq_lens[b] / partition_size) take part:
+ *     M = max_p lse_p,  w_p = exp(lse_p - M),
+ *     out = sum_p w_p o_p / sum_p w_p,  out_lse = M + ln sum_p w_p.
+ * A sequence with no partition gets out = 0 and out_lse = -inf.
+ * out_dtype is PA_F32 or PA_BF16 (round to nearest even); out_lse may be NULL.
+ */
+int pa_merge_partitions(void* out, int out_dtype, float* out_lse,
+                        const float* partial_out, const float* partial_lse,
+                        const int32_t* seq_lens, int partition_size, int max_partitions,
+                        int num_seqs, int num_q_heads, int head_dim, void* stream);
+
+/*
+ * Causal chunked prefill over a paged context.  Chunk c owns query rows
+ * cu_q_lens[c] .. cu_q_lens[c+1]-1 of `q`; its sequence has seq_lens[c]
+ * tokens in the cache (the context followed by the chunk itself), so with
+ * ctx = seq_lens[c] - q_len_c, query i of the chunk sits at position ctx + i
+ * and attends to keys 0 .. ctx + i (the causal mask aligned to the
+ * bottom-right of the score matrix).  Several block-table rows may reference
+ * the same physical blocks (a shared prefix).  max_q_len is the host-side
+ * bound on every chunk's length; it sizes the grid.  out_lse (fp32
+ * [total_q, num_q_heads], natural log) may be NULL.
+ */
+int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
+                     const int32_t* cu_q_lens, int total_q, int max_q_len,
+                     const void* k_cache, const void* v_cache, int kv_dtype,
+                     const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int num_chunks,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, float scale, const float* k_scale,
+                     const float* v_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,204 @@
+"""ctypes binding of libpa.so: torch tensors -> device pointers + the current
+HIP stream.  Argument marshalling only; every step of the computation runs in
+the library's kernels.  There is no CPU path: if libpa.so is missing, or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
+                4: "PA_ERR_ALIGN", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP"}
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+# argument lists of the exported functions, in include/pa.h order
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [_i]),
+    "pa_version": (_i, []),
+    "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "pa_decode": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f,
+                       _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "pa_decode_partitions": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i,
+                                  _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
+    "pa_merge_partitions": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "pa_prefill_chunk": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
+                              _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
+}
+
+
+class PAError(RuntimeError):
+    """A libpa call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_22_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.pa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PAError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, kv: bool) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if kv and t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libpa has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                          partition_size: int) -> int:
+    return int(lib.pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                            partition_size))
+
+
+def _kv_dims(q, k_cache, v_cache):
+    B, Hq, d = q.shape
+    NB, Hkv, bs, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != (NB, Hkv, d, bs):
+        raise ValueError("k_cache must be [NB, Hkv, bs, d] and v_cache [NB, Hkv, d, bs]")
+    return B, Hq, d, NB, Hkv, bs
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
+           scale: Optional[float] = None, partition_size: int = 0, k_scale=None, v_scale=None,
+           out=None, workspace=None):
+    """Decode attention (pa_decode).  Returns ``out`` [B, Hq, d] in q's dtype."""
+    torch = _torch()
+    B, Hq, d, NB, Hkv, bs = _kv_dims(q, k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = d ** -0.5
+    ws_need = decode_workspace_size(B, Hq, d, max_seq_len, partition_size)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode(_dev(out, "out"), _dev(q, "q"), _dtype_code(q, False),
+                       _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache, True),
+                       _dev(block_table, "block_table"), block_table.shape[1],
+                       _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d, bs, NB, float(scale),
+                       _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                       int(partition_size), int(max_seq_len),
+                       _dev(workspace, "workspace"), ws_bytes, _stream(q))
+    _check("pa_decode", st)
+    return out
+
+
+def decode_partitions(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
+                      partition_size: int, scale: Optional[float] = None, k_scale=None,
+                      v_scale=None, partial_out=None, partial_lse=None):
+    """Split-KV partition kernel only (pa_decode_partitions).  Returns
+    (partial_out [B, Hq, Pmax, d] fp32, partial_lse [B, Hq, Pmax] fp32)."""
+    torch = _torch()
+    B, Hq, d, NB, Hkv, bs = _kv_dims(q, k_cache, v_cache)
+    pmax = max(1, -(-int(max_seq_len) // int(partition_size)))
+    if partial_out is None:
+        partial_out = torch.empty((B, Hq, pmax, d), dtype=torch.float32, device=q.device)
+    if partial_lse is None:
+        partial_lse = torch.empty((B, Hq, pmax), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.pa_decode_partitions(_dev(partial_out, "partial_out"), _dev(partial_lse, "partial_lse"),
+                                  partial_out.shape[2], _dev(q, "q"), _dtype_code(q, False),
+                                  _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                  _dtype_code(k_cache, True), _dev(block_table, "block_table"),
+                                  block_table.shape[1], _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d,
+                                  bs, NB, float(scale), _dev(k_scale, "k_scale"),
+                                  _dev(v_scale, "v_scale"), int(partition_size), int(max_seq_len),
+                                  _stream(q))
+    _check("pa_decode_partitions", st)
+    return partial_out, partial_lse
+
+
+def merge_partitions(partial_out, partial_lse, seq_lens, *, partition_size: int,
+                     out_dtype=None, out=None, out_lse=None, want_lse: bool = False):
+    """Log-sum-exp merge (pa_merge_partitions).  Returns out, or (out, lse)."""
+    torch = _torch()
+    B, Hq, pmax, d = partial_out.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=partial_out.device)
+    if want_lse and out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=partial_out.device)
+    st = lib.pa_merge_partitions(_dev(out, "out"), _dtype_code(out, False), _dev(out_lse, "out_lse"),
+                                 _dev(partial_out, "partial_out"), _dev(partial_lse, "partial_lse"),
+                                 _dev(seq_lens, "seq_lens"), int(partition_size), pmax, B, Hq, d,
+                                 _stream(partial_out))
+    _check("pa_merge_partitions", st)
+    return (out, out_lse) if want_lse else out
+
+
+def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, *, max_q_len: int,
+                  scale: Optional[float] = None, k_scale=None, v_scale=None, out=None,
+                  out_lse=None, want_lse: bool = False):
+    """Causal chunked prefill (pa_prefill_chunk).  Returns out [total_q, Hq, d]
+    (and lse [total_q, Hq] when want_lse)."""
+    torch = _torch()
+    total_q, Hq, d, NB, Hkv, bs = _kv_dims(q, k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and out_lse is None:
+        out_lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.pa_prefill_chunk(_dev(out, "out"), _dev(out_lse, "out_lse"), _dev(q, "q"),
+                              _dtype_code(q, False), _dev(cu_q_lens, "cu_q_lens"), total_q,
+                              int(max_q_len), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dtype_code(k_cache, True), _dev(block_table, "block_table"),
+                              block_table.shape[1], _dev(seq_lens, "seq_lens"), seq_lens.shape[0],
+                              Hq, Hkv, d, bs, NB, float(scale), _dev(k_scale, "k_scale"),
+                              _dev(v_scale, "v_scale"), _stream(q))
+    _check("pa_prefill_chunk", st)
+    return (out, out_lse) if want_lse else out

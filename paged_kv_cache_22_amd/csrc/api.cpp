@@ -1,0 +1,287 @@
+// C-ABI front end of libpa.so: argument validation and dispatch.  Host code
+// only; it never touches device memory, never synchronises and never
+// allocates.  Every check runs before the first launch, so a rejected call
+// enqueues nothing.  The contract is documented in include/pa.h.
+#include "../../include/pa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxGroup = 16;          // q-heads per kv-head handled by one wave
+constexpr int kMaxGridY = 65535;
+constexpr size_t kRegionAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int dtype_ok(int q_dtype, int kv_dtype) {
+    if (q_dtype < PA_F32 || q_dtype > PA_BF16) return PA_ERR_DTYPE;
+    if (kv_dtype < PA_F32 || kv_dtype > PA_FP8_E4M3) return PA_ERR_DTYPE;
+    const bool ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) ||
+                    (q_dtype == PA_BF16 && (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3));
+    return ok ? PA_OK : PA_ERR_DTYPE;
+}
+
+// checks shared by decode and prefill
+int common_checks(const void* q, const void* k_cache, const void* v_cache, int q_dtype, int kv_dtype,
+                  const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  float scale, const float* k_scale, const float* v_scale) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens) return PA_ERR_NULL;
+    int st = dtype_ok(q_dtype, kv_dtype);
+    if (st != PA_OK) return st;
+    if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks < 0 || max_blocks_per_seq <= 0)
+        return PA_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return PA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+int decode_checks(const void* q, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+                  const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                  int partition_size, int max_seq_len) {
+    int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           scale, k_scale, v_scale);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || max_seq_len < 0) return PA_ERR_SHAPE;
+    if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+    if (partition_size < 0) return PA_ERR_SHAPE;
+    if (partition_size % block_size != 0) return PA_ERR_UNSUPPORTED;
+    if (partition_size > 0) {
+        const long long parts = ((long long)max_seq_len + partition_size - 1) / partition_size;
+        if (parts > kMaxGridY) return PA_ERR_UNSUPPORTED;
+    }
+    return PA_OK;
+}
+
+pa::DecodeArgs make_decode_args(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                                int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
+                                const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, float scale, const float* k_scale,
+                                const float* v_scale) {
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_dtype = kv_dtype;
+    a.block_table = block_table;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.scale = scale;
+    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    return a;
+}
+
+int hip_status(int e) { return e == 0 ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+        case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is negative, inconsistent or too large";
+        case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown or unsupported dtype combination";
+        case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        case PA_ERR_UNSUPPORTED:
+            return "PA_ERR_UNSUPPORTED: head_dim, block_size, group size or partition size not supported";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+        case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime rejected a launch";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+int pa_version(void) { return 100; }
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                                int partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size < 0)
+        return 0;
+    if (partition_size == 0) return 0;
+    const size_t parts = ((size_t)max_seq_len + partition_size - 1) / partition_size;
+    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    return round_up(rows * head_dim * sizeof(float), kRegionAlign) +
+           round_up(rows * sizeof(float), kRegionAlign);
+}
+
+int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partitions, const void* q,
+                         int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+                         const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int num_blocks, float scale, const float* k_scale,
+                         const float* v_scale, int partition_size, int max_seq_len, void* stream) {
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (partition_size == 0) return PA_ERR_UNSUPPORTED;
+    if (!partial_out || !partial_lse) return PA_ERR_NULL;
+    if (!aligned16(partial_out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u)) return PA_ERR_ALIGN;
+    const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
+    if (max_partitions < parts) return PA_ERR_SHAPE;
+    if (num_seqs == 0 || parts == 0) return PA_OK;
+    pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
+                                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, scale, k_scale, v_scale);
+    a.part_out = partial_out;
+    a.part_lse = partial_lse;
+    a.max_parts = max_partitions;
+    a.partition_blocks = partition_size / block_size;
+    a.grid_parts = parts;
+    return hip_status(pa::launch_decode(a, stream));
+}
+
+int pa_merge_partitions(void* out, int out_dtype, float* out_lse, const float* partial_out,
+                        const float* partial_lse, const int32_t* seq_lens, int partition_size,
+                        int max_partitions, int num_seqs, int num_q_heads, int head_dim, void* stream) {
+    if (!out || !partial_out || !partial_lse || !seq_lens) return PA_ERR_NULL;
+    if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_partitions < 0 || partition_size <= 0)
+        return PA_ERR_SHAPE;
+    if ((long long)num_seqs * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(out) || !aligned16(partial_out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u) ||
+        (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(out_lse) & 3u))
+        return PA_ERR_ALIGN;
+    if (num_seqs == 0) return PA_OK;
+    pa::MergeArgs m{};
+    m.out = out;
+    m.out_dtype = out_dtype;
+    m.out_lse = out_lse;
+    m.part_out = partial_out;
+    m.part_lse = partial_lse;
+    m.seq_lens = seq_lens;
+    m.partition_size = partition_size;
+    m.max_parts = max_partitions;
+    m.num_seqs = num_seqs;
+    m.num_q_heads = num_q_heads;
+    m.head_dim = head_dim;
+    return hip_status(pa::launch_merge(m, stream));
+}
+
+int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+              int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
+              const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, float scale, const float* k_scale,
+              const float* v_scale, int partition_size, int max_seq_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (!out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
+                                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, scale, k_scale, v_scale);
+    if (partition_size == 0) {
+        if (num_seqs == 0) return PA_OK;
+        a.out = out;
+        a.partition_blocks = 0;
+        a.grid_parts = 1;
+        return hip_status(pa::launch_decode(a, stream));
+    }
+    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                                 partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
+    if (num_seqs == 0) return PA_OK;
+    const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
+    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    float* part_out = reinterpret_cast<float*>(workspace);
+    float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                               round_up(rows * head_dim * sizeof(float), kRegionAlign));
+    if (parts > 0) {
+        a.part_out = part_out;
+        a.part_lse = part_lse;
+        a.max_parts = parts;
+        a.partition_blocks = partition_size / block_size;
+        a.grid_parts = parts;
+        st = hip_status(pa::launch_decode(a, stream));
+        if (st != PA_OK) return st;
+    }
+    pa::MergeArgs m{};
+    m.out = out;
+    m.out_dtype = q_dtype;
+    m.out_lse = nullptr;
+    m.part_out = part_out;
+    m.part_lse = part_lse;
+    m.seq_lens = seq_lens;
+    m.partition_size = partition_size;
+    m.max_parts = parts;
+    m.num_seqs = num_seqs;
+    m.num_q_heads = num_q_heads;
+    m.head_dim = head_dim;
+    return hip_status(pa::launch_merge(m, stream));
+}
+
+int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, const int32_t* cu_q_lens,
+                     int total_q, int max_q_len, const void* k_cache, const void* v_cache,
+                     int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int num_chunks, int num_q_heads, int num_kv_heads,
+                     int head_dim, int block_size, int num_blocks, float scale, const float* k_scale,
+                     const float* v_scale, void* stream) {
+    int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           scale, k_scale, v_scale);
+    if (st != PA_OK) return st;
+    if (!out || !cu_q_lens) return PA_ERR_NULL;
+    if (!aligned16(out) || (reinterpret_cast<uintptr_t>(cu_q_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(out_lse) & 3u))
+        return PA_ERR_ALIGN;
+    if (num_chunks < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_SHAPE;
+    if ((long long)num_chunks * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const long long groups = ((long long)max_q_len * (num_q_heads / num_kv_heads) + 31) / 32;
+    if (groups > kMaxGridY) return PA_ERR_UNSUPPORTED;
+    if (num_chunks == 0 || max_q_len == 0) return PA_OK;
+    pa::PrefillArgs a{};
+    a.out = out;
+    a.out_lse = out_lse;
+    a.q = q;
+    a.cu_q_lens = cu_q_lens;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.num_chunks = num_chunks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale = scale;
+    return hip_status(pa::launch_prefill(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI front end (api.cpp, host only) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+    // outputs: exactly one of (out) or (part_out, part_lse) is used
+    void* out;            // [B, Hq, D] in q's dtype (one-pass mode)
+    float* part_out;      // [B, Hq, max_parts, D]     (split mode)
+    float* part_lse;      // [B, Hq, max_parts]
+    int max_parts;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const float* k_scale;
+    const float* v_scale;
+    int q_dtype;          // pa_dtype
+    int kv_dtype;         // pa_dtype
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks_per_seq;
+    int partition_blocks; // blocks per partition; 0 = whole sequence in one pass
+    int grid_parts;       // partitions in the grid (1 in one-pass mode)
+    float scale;
+};
+
+struct MergeArgs {
+    void* out;
+    int out_dtype;
+    float* out_lse;       // nullable
+    const float* part_out;
+    const float* part_lse;
+    const int32_t* seq_lens;
+    int partition_size, max_parts;
+    int num_seqs, num_q_heads, head_dim;
+};
+
+struct PrefillArgs {
+    void* out;
+    float* out_lse;       // nullable
+    const void* q;
+    const int32_t* cu_q_lens;
+    int total_q, max_q_len;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const float* k_scale;
+    const float* v_scale;
+    int q_dtype, kv_dtype;
+    int num_chunks, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks_per_seq;
+    float scale;
+};
+
+// Each returns 0 on success or the hipError_t of a failed launch.
+int launch_decode(const DecodeArgs& a, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+int launch_prefill(const PrefillArgs& a, void* stream);
+
+}  // namespace pa

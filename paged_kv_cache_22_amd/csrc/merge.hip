@@ -1,0 +1,86 @@
+// Log-sum-exp merge of split-KV decode partials.  gfx950 / CDNA4.
+//
+// Partition p of a sequence yields o_p (softmax-normalised over its tokens)
+// and lse_p = ln sum exp(s) over the same tokens.  Attention over the union of
+// the partitions is sum_p w_p o_p / sum_p w_p with w_p = exp(lse_p - M),
+// M = max_p lse_p (the standard combination of softmax pieces; the pages give
+// no merge rule of their own).  One wave per (sequence, q-head); every lane
+// owns D / 64 consecutive output dims, so each partial row is read as one
+// contiguous 256- or 512-byte run.
+#include "device.h"
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+__device__ __forceinline__ float wave_max(float x) { return group_max4(row_max16(x)); }
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
+    constexpr int V = D / 64;  // dims per lane
+    const int lane = threadIdx.x;
+    const int Hq = a.num_q_heads;
+    const int qh = blockIdx.x % Hq;
+    const int b = blockIdx.x / Hq;
+    const size_t row = (size_t)b * Hq + qh;
+    const int L = a.seq_lens[b];
+    const int np = min((L + a.partition_size - 1) / a.partition_size, a.max_parts);
+    const float* lse = a.part_lse + row * a.max_parts;
+    const float* po = a.part_out + row * a.max_parts * D + lane * V;
+
+    float M = -INFINITY;
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, lse[p]);
+    M = wave_max(M);
+
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    float den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int p = 0; p < np; ++p) {
+            // difference first: exactly 0 for the largest lse, whatever the
+            // compiler fuses, so a lone partition passes through unchanged
+            const float w = fast_exp2((lse[p] - M) * kLog2e);
+            den += w;
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] += w * po[(size_t)p * D + v];
+        }
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    if constexpr (OUT_BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * D + lane * V;
+        if constexpr (V == 2) {
+            *reinterpret_cast<unsigned*>(o) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        } else {
+            __bf16 x = (__bf16)(acc[0] * inv);
+            *o = bitcast<uint16_t>(x);
+        }
+    } else {
+        float* o = reinterpret_cast<float*>(a.out) + row * D + lane * V;
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = acc[v] * inv;
+    }
+    if (a.out_lse && lane == 0)
+        a.out_lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_d(const MergeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.num_seqs * a.num_q_heads));
+    if (a.out_dtype == 1)
+        hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_merge(const MergeArgs& a, void* stream) {
+    if (a.num_seqs == 0) return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return (int)(a.head_dim == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s));
+}
+
+}  // namespace pa

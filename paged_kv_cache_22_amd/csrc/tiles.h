@@ -1,0 +1,177 @@
+// Per-KV-dtype access to one (block, kv-head) tile of the paged cache, in the
+// MFMA operand layouts the attention kernels use.  gfx950 / CDNA4.
+//
+// A K tile is [16 tokens][D] (token-major), a V tile is [D][16 tokens]
+// (dim-major), so that both products of attention read their operands as
+// contiguous runs: the score product S^T = K . Q^T contracts over dims, which
+// run along a K row, and the output product O^T = V^T . P^T contracts over
+// tokens, which run along a V row.
+#pragma once
+
+#include "device.h"
+
+namespace pa {
+
+constexpr int kBS = 16;  // tokens per cache block
+
+// ---------------------------------------------------------------------------
+// Per-KV-dtype tile access.  For every kind:
+//   Regs  the lane's share of one block's K and V tile
+//   QOp   the lane's share of Q^T, the B operand of the score MFMAs
+//   load  issues the global loads of one block
+//   qk    S^T fragment: lane (r, c) gets scores of head r, tokens 4c..4c+3
+//   pv    acc[n] += V^T[16n..16n+15, tokens] . P^T for this block
+// ---------------------------------------------------------------------------
+template <int KIND, int D> struct Tile;
+
+template <int D> struct Tile<KV_BF16, D> {
+    static constexpr int kTileBytes = kBS * D * 2;
+    static constexpr int KL = D / 32;  // 16-byte K loads per lane = score MFMAs
+    static constexpr int NT = D / 16;  // 16-dim tiles of the output
+    struct Regs { u32x4 k[KL]; u32x2 v[NT]; };
+    struct QOp { u32x4 b[KL]; };
+
+    // k-slot (c, e) of MFMA i stands for dim (4i + c) * 8 + e
+    __device__ static void load_q(QOp& Q, const uint16_t* qrow, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            Q.b[i] = qrow ? ld16(qrow + (4 * i + c) * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * (D * 2) + (4 * i + c) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld8(vt + (16 * n + r) * (kBS * 2) + c * 8);
+    }
+    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+        f32x4 s = zero4();
+#pragma unroll
+        for (int i = 0; i < KL; ++i) s = mfma_16x16x32_bf16(R.k[i], Q.b[i], s);
+        return s;
+    }
+    __device__ static void mask_v(Regs& R, int c, int valid) {
+        const int t0 = 4 * c;
+        const unsigned mx = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
+        const unsigned my = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) { R.v[n].x &= mx; R.v[n].y &= my; }
+    }
+    __device__ static void pv(const Regs& R, const float p[4], f32x4* acc) {
+        u32x2 pb;
+        pb.x = pack_bf16x2(p[0], p[1]);
+        pb.y = pack_bf16x2(p[2], p[3]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(R.v[n], pb, acc[n]);
+    }
+};
+
+template <int D> struct Tile<KV_FP8, D> {
+    static constexpr int kTileBytes = kBS * D;
+    static constexpr int KL = D / 64;  // 16-byte K loads per lane, 16 codes = two MFMAs each
+    static constexpr int NT = D / 16;
+    struct Regs { u32x4 k[KL]; unsigned v[NT]; };
+    struct QOp { u32x4 b[2 * KL]; };
+
+    // k-slot (c, e) of MFMA 2i + h stands for dim (4i + c) * 16 + 8h + e
+    __device__ static void load_q(QOp& Q, const uint16_t* qrow, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                Q.b[2 * i + hh] = qrow ? ld16(qrow + (4 * i + c) * 16 + 8 * hh)
+                                       : u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * D + (4 * i + c) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld4(vt + (16 * n + r) * kBS + c * 4);
+    }
+    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+        f32x4 s = zero4();
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const u32x2 a0 = fp8x4_to_bf16x4(R.k[i].x), a1 = fp8x4_to_bf16x4(R.k[i].y);
+            const u32x2 a2 = fp8x4_to_bf16x4(R.k[i].z), a3 = fp8x4_to_bf16x4(R.k[i].w);
+            s = mfma_16x16x32_bf16(u32x4{a0.x, a0.y, a1.x, a1.y}, Q.b[2 * i], s);
+            s = mfma_16x16x32_bf16(u32x4{a2.x, a2.y, a3.x, a3.y}, Q.b[2 * i + 1], s);
+        }
+        return s;
+    }
+    __device__ static void mask_v(Regs& R, int c, int valid) {
+        const int t0 = 4 * c;
+        unsigned mk = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mk |= (t0 + e < valid ? 0xffu : 0u) << (8 * e);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] &= mk;  // code 0x00 is +0
+    }
+    __device__ static void pv(const Regs& R, const float p[4], f32x4* acc) {
+        u32x2 pb;
+        pb.x = pack_bf16x2(p[0], p[1]);
+        pb.y = pack_bf16x2(p[2], p[3]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(fp8x4_to_bf16x4(R.v[n]), pb, acc[n]);
+    }
+};
+
+template <int D> struct Tile<KV_F32, D> {
+    static constexpr int kTileBytes = kBS * D * 4;
+    static constexpr int KL = D / 16;  // 16-byte K loads per lane, four MFMAs each
+    static constexpr int NT = D / 16;
+    struct Regs { u32x4 k[KL]; u32x4 v[NT]; };
+    struct QOp { u32x4 b[KL]; };
+
+    // k-slot c of MFMA 4i + e stands for dim (4i + c) * 4 + e
+    __device__ static void load_q(QOp& Q, const float* qrow, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            Q.b[i] = qrow ? ld16(qrow + (4 * i + c) * 4) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * (D * 4) + (4 * i + c) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld16(vt + (16 * n + r) * (kBS * 4) + c * 16);
+    }
+    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+        f32x4 s = zero4();
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s = mfma_16x16x4_f32(__uint_as_float(R.k[i][e]), __uint_as_float(Q.b[i][e]), s);
+        return s;
+    }
+    __device__ static void mask_v(Regs& R, int c, int valid) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * c + e >= valid)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) R.v[n][e] = 0u;
+    }
+    // PV MFMA e: k-slot c stands for token 4c + e
+    __device__ static void pv(const Regs& R, const float p[4], f32x4* acc) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[n] = mfma_16x16x4_f32(__uint_as_float(R.v[n][e]), p[e], acc[n]);
+    }
+};
+
+template <int KIND> struct QType { using T = uint16_t; };   // bf16 bits
+template <> struct QType<KV_F32> { using T = float; };
+
+// store 4 consecutive output values of one row
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+    u32x2 w;
+    w.x = pack_bf16x2(a, b);
+    w.y = pack_bf16x2(c, d);
+    *reinterpret_cast<u32x2*>(p) = w;
+}
+
+}  // namespace pa

@@ -1,0 +1,52 @@
+"""Shared helpers of the GPU parity tests: move seeded workloads to the GPU,
+run the library through its binding, compare with the oracle."""
+import numpy as np
+import torch
+
+from workloads.device import Dev, dev  # noqa: F401  (re-exported for the tests)
+
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}          # graded max-abs error
+# internal gate relative to the largest reference magnitude: catches errors the
+# absolute bar misses at long contexts, where |out| is small
+REL = {"f32": 2e-6, "bf16": 2.0 ** -7, "fp8": 2.0 ** -7}
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_decode(d: Dev, partition_size=None, **kw):
+    import paged_kv_cache_22_amd as pa
+    wl = d.wl
+    P = wl.partition_size if partition_size is None else partition_size
+    out = pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                    partition_size=P, k_scale=d.ks, v_scale=d.vs, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_prefill(d: Dev, want_lse=False):
+    import paged_kv_cache_22_amd as pa
+    wl = d.wl
+    r = pa.prefill_chunk(d.q, d.cu, d.k, d.v, d.bt, d.sl, max_q_len=wl.max_q_len, scale=wl.scale,
+                         k_scale=d.ks, v_scale=d.vs, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return r
+
+
+def compare(got, ref, dtype, what="", mask=None):
+    """Max-abs error against the oracle, the graded bar and the relative gate.
+    ``mask`` selects the rows the oracle computed (others are NaN there)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    assert np.isfinite(ref).all(), "oracle rows missing"
+    assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    print(f"[parity] {what}: max_abs_err={err:.3e} max|ref|={scale:.3e} "
+          f"tol={TOL[dtype]:.0e} rel_gate={REL[dtype] * scale:.3e}", flush=True)
+    assert err <= TOL[dtype], f"{what}: max-abs error {err} > {TOL[dtype]}"
+    assert err <= REL[dtype] * scale + 1e-30, f"{what}: error {err} above {REL[dtype]}*max|ref|"
+    return err

@@ -1,0 +1,130 @@
+"""Causal chunked prefill (and the mixed C4 step) against the fp64 oracle,
+through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import Dev, compare, f64, run_decode, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_prefill(wl, items=None):
+    return oracle.prefill_chunk(wl.q, wl.cu_q_lens, wl.k_cache, wl.v_cache, wl.block_table,
+                                wl.seq_lens, wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale,
+                                wl.v_scale, items=items)
+
+
+def rows_mask(ref):
+    return ~np.isnan(ref[..., 0])
+
+
+@pytest.mark.parametrize("kv,d_head", [("f32", 64), ("f32", 128), ("bf16", 128), ("bf16", 64),
+                                       ("fp8", 128)])
+def test_ragged_chunks(kv, d_head):
+    qd = "f32" if kv == "f32" else "bf16"
+    wl = W.prefill_workload(seed=200 + d_head, q_lens=[5, 17, 40, 1, 64, 33],
+                            ctx_lens=[0, 33, 9, 100, 64, 0], num_q_heads=8, num_kv_heads=2,
+                            head_dim=d_head, q_dtype=qd, kv_dtype=kv)
+    d = Dev(wl)
+    ref, ref_lse = oracle_prefill(wl)
+    got, lse = run_prefill(d, want_lse=True)
+    compare(f64(got), ref, kv, f"prefill ragged {kv} d={d_head}")
+    assert np.abs(f64(lse) - ref_lse).max() < 1e-3
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 16])
+def test_group_sizes(G):
+    wl = W.prefill_workload(seed=210 + G, q_lens=[37, 100], ctx_lens=[50, 0], num_q_heads=2 * G,
+                            num_kv_heads=2, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    ref, _ = oracle_prefill(wl)
+    compare(f64(run_prefill(Dev(wl))), ref, "bf16", f"prefill G={G}")
+
+
+def test_c4_mixed_step():
+    wl = W.config4()
+    # decode rows of the mixed step
+    dd = Dev(wl.decode)
+    ref_d, _ = oracle.decode(wl.decode.q, wl.decode.k_cache, wl.decode.v_cache,
+                             wl.decode.block_table, wl.decode.seq_lens, wl.decode.scale,
+                             "bf16", "bf16")
+    compare(f64(run_decode(dd)), ref_d, "bf16", "C4 decode rows")
+    # prefill chunks over the shared 2048-token prefix (sampled (chunk, kv-head) pairs)
+    pre = wl.prefill
+    dp = Dev(pre)
+    got = f64(run_prefill(dp))
+    items = [(c, h) for c in range(4) for h in (0, 5)] + [(2, h) for h in (1, 2, 3, 4, 6, 7)]
+    ref, _ = oracle_prefill(pre, items)
+    compare(got, ref, "bf16", "C4 prefill sampled", mask=rows_mask(ref))
+    assert np.isfinite(got).all()
+
+
+def test_causal_boundary_exact_selection():
+    """Keys all -1 except key tau (+1), q = 8: rows at positions >= tau return
+    V[tau] exactly; rows before tau see only equal scores, i.e. the mean of
+    V over keys 0..pos."""
+    ctx, n = 40, 50
+    wl = W.prefill_workload(seed=220, q_lens=[n], ctx_lens=[ctx], num_q_heads=8, num_kv_heads=2,
+                            head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    rng = np.random.default_rng(3)
+    wl.v_cache[:] = W.to_bf16_bits(rng.integers(0, 16, wl.v_cache.shape).astype(np.float32))
+    wl.q[:] = W.to_bf16_bits(np.full(wl.q.shape, 8, np.float32))
+    L = ctx + n
+    V = np.stack([oracle.gather_kv(wl.k_cache, wl.v_cache, wl.block_table[0], L, h, "bf16")[1]
+                  for h in range(2)])                       # [Hkv, L, d]
+    for tau in (0, 15, 16, 39, 40, 41, 63, 64, 89):
+        k = -np.ones(wl.k_cache.shape, np.float32)
+        phys = int(wl.block_table[0, tau // 16])
+        k[phys, :, tau % 16, :] = 1.0
+        wl.k_cache[:] = W.to_bf16_bits(k)
+        got = f64(run_prefill(Dev(wl)))
+        for i in range(n):
+            pos = ctx + i
+            for j in range(8):
+                h = j // 4
+                if pos >= tau:
+                    assert np.array_equal(got[i, j], V[h, tau]), (tau, i, j)
+                else:
+                    assert np.abs(got[i, j] - V[h, :pos + 1].mean(0)).max() <= 2.0 ** -8 * 16, (tau, i, j)
+
+
+def test_shared_prefix_bit_identical_to_private_copies():
+    n_chunks, prefix_blocks = 3, 6
+    wl = W.prefill_workload(seed=230, q_lens=[70, 16, 33], ctx_lens=[96, 96, 96], num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    private = run_prefill(Dev(wl)).clone()
+    # point every chunk's first 6 table entries at chunk 0's prefix blocks, after
+    # copying chunk 0's prefix contents into the other chunks' prefix blocks
+    for c in range(1, n_chunks):
+        for j in range(prefix_blocks):
+            wl.k_cache[wl.block_table[c, j]] = wl.k_cache[wl.block_table[0, j]]
+            wl.v_cache[wl.block_table[c, j]] = wl.v_cache[wl.block_table[0, j]]
+    private = run_prefill(Dev(wl)).clone()
+    shared_tab = wl.block_table.copy()
+    shared_tab[1:, :prefix_blocks] = wl.block_table[0, :prefix_blocks]
+    wl.block_table = shared_tab
+    shared = run_prefill(Dev(wl))
+    assert torch.equal(shared, private)
+
+
+def test_chunked_equals_whole_sequence():
+    """One sequence of 300 tokens fed as chunks of 64 (as in the pages' parity
+    runs) gives the same rows as one chunk over the whole sequence."""
+    L = 300
+    whole = W.prefill_workload(seed=240, q_lens=[L], ctx_lens=[0], num_q_heads=8, num_kv_heads=2,
+                               head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    ref = f64(run_prefill(Dev(whole)))
+    bounds = list(range(0, L, 64)) + [L]
+    q_lens = [b - a for a, b in zip(bounds[:-1], bounds[1:])]
+    chunks = W.PrefillWorkload(
+        name="chunks", q=whole.q, cu_q_lens=np.array(bounds, np.int32),
+        k_cache=whole.k_cache, v_cache=whole.v_cache,
+        block_table=np.repeat(whole.block_table, len(q_lens), axis=0),
+        seq_lens=np.array(bounds[1:], np.int32), q_dtype="bf16", kv_dtype="bf16",
+        scale=whole.scale)
+    got = f64(run_prefill(Dev(chunks)))
+    assert np.abs(got - ref).max() <= 2.0 ** -8 * max(1.0, np.abs(ref).max())
+    ref_o, _ = oracle_prefill(whole)
+    compare(got, ref_o, "bf16", "64-token chunks vs oracle")

@@ -22,9 +22,10 @@ cache and say the platform fixes the cache layout (vllm-metal architecture
 article, sections 二 and 四) but never give one; the layout above is this
 library's choice and is used identically by every consumer.
 
-Draw order per workload (one ``numpy.random.default_rng(seed)`` stream):
-sequence lengths -> pool permutation -> q -> K pool -> V pool.  K and V are
-drawn in fp32 N(0, 1) in chunks of 4096 blocks.  Sequence ``b`` takes the
+Draw order per workload: ``numpy.random.default_rng(seed)`` draws the
+sequence lengths, then the pool permutation, then q; the K and V pools are
+drawn in fp32 N(0, 1) in chunks of 1024 blocks, chunk k of K from
+``default_rng([seed, 1, k])`` and of V from ``default_rng([seed, 2, k])``.  Sequence ``b`` takes the
 next ``ceil(L_b / block_size)`` entries of the permutation as its block-table
 row; unused table entries are padding (``-1`` by default).
 """
@@ -32,13 +33,16 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
 
 BLOCK_SIZE = 16
 FP8_MAX = 448.0  # OCP e4m3fn largest finite value; scale rule amax / 448
-_CHUNK_BLOCKS = 4096
+_CHUNK_BLOCKS = 1024
+_THREADS = min(16, os.cpu_count() or 1)
 
 __all__ = [
     "DecodeWorkload", "PrefillWorkload", "MixedWorkload",
@@ -199,27 +203,46 @@ class MixedWorkload:
 # ---------------------------------------------------------------------------
 # drawing
 # ---------------------------------------------------------------------------
-def _draw_pool(rng, num_blocks, num_kv_heads, head_dim, block_size, dtype):
-    """Draw one N(0,1) pool of num_blocks tiles in chunks; returns storage array
-    (f32 or bf16 bits) or, for fp8, the fp32 pool (quantised later)."""
+def _draw_pool(seed, stream, num_blocks, num_kv_heads, head_dim, block_size, dtype):
+    """Draw one N(0,1) pool of num_blocks tiles; returns the storage array
+    (f32 or bf16 bits) or, for fp8, the fp32 pool (quantised later).
+
+    Chunk k of 4096 blocks comes from its own generator
+    ``default_rng([seed, stream, k])``, so chunks are drawn in parallel
+    threads and the result does not depend on the thread count."""
     tile = num_kv_heads * head_dim * block_size
-    if dtype == "bf16":
-        out = np.empty(num_blocks * tile, dtype=np.uint16)
-    else:
-        out = np.empty(num_blocks * tile, dtype=np.float32)
-    for b0 in range(0, num_blocks, _CHUNK_BLOCKS):
+    out = np.empty(num_blocks * tile, dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def one(k):
+        b0 = k * _CHUNK_BLOCKS
         b1 = min(num_blocks, b0 + _CHUNK_BLOCKS)
-        x = rng.standard_normal((b1 - b0) * tile, dtype=np.float32)
+        x = np.random.default_rng([seed, stream, k]).standard_normal((b1 - b0) * tile,
+                                                                      dtype=np.float32)
         out[b0 * tile:b1 * tile] = to_bf16_bits(x) if dtype == "bf16" else x
+
+    n_chunks = -(-num_blocks // _CHUNK_BLOCKS)
+    with ThreadPoolExecutor(max_workers=min(_THREADS, max(1, n_chunks))) as ex:
+        list(ex.map(one, range(n_chunks)))
     return out
 
 
 def _quantise_pool_fp8(pool_f32, num_kv_heads):
-    """Per-kv-head amax/448 scale, then e4m3fn codes.  pool: [NB, Hkv, ...]."""
+    """Per-kv-head amax/448 scale, then e4m3fn codes.  pool: [NB, Hkv, ...].
+    Works in block chunks on a thread pool (numpy and torch release the GIL)."""
     nb = pool_f32.shape[0]
-    amax = np.abs(pool_f32.reshape(nb, num_kv_heads, -1)).max(axis=(0, 2))
+    flat = pool_f32.reshape(nb, num_kv_heads, -1)
+    chunks = [(b0, min(nb, b0 + _CHUNK_BLOCKS)) for b0 in range(0, nb, _CHUNK_BLOCKS)]
+    with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+        parts = list(ex.map(lambda c: np.abs(flat[c[0]:c[1]]).max(axis=(0, 2)), chunks))
+    amax = np.max(np.stack(parts), axis=0)
     scale = (amax.astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
-    codes = to_fp8_codes(pool_f32, scale, axis_scale=1)
+    codes = np.empty(pool_f32.shape, dtype=np.uint8)
+
+    def one(c):
+        codes[c[0]:c[1]] = to_fp8_codes(pool_f32[c[0]:c[1]], scale, axis_scale=1)
+
+    with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+        list(ex.map(one, chunks))
     return codes, scale
 
 
@@ -233,9 +256,9 @@ def _tables_from_perm(perm, lens, block_size, max_blocks, pad):
     return table, pos
 
 
-def _make_pools(rng, nb, hkv, d, bs, kv_dtype):
-    k = _draw_pool(rng, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
-    v = _draw_pool(rng, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
+def _make_pools(seed, nb, hkv, d, bs, kv_dtype):
+    k = _draw_pool(seed, 1, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
+    v = _draw_pool(seed, 2, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
     k = k.reshape(nb, hkv, bs, d)
     v = v.reshape(nb, hkv, d, bs)
     ks = vs = None
@@ -269,7 +292,7 @@ def decode_workload(*, seed: int, num_seqs: int, num_q_heads: int, num_kv_heads:
     max_blocks = max(1, -(-int(lens.max(initial=0)) // block_size))
     table, _ = _tables_from_perm(perm, lens, block_size, max_blocks, pad)
     q = _draw_q(rng, (num_seqs, num_q_heads, head_dim), q_dtype)
-    k, v, ks, vs = _make_pools(rng, nb, num_kv_heads, head_dim, block_size, kv_dtype)
+    k, v, ks, vs = _make_pools(seed, nb, num_kv_heads, head_dim, block_size, kv_dtype)
     return DecodeWorkload(name=name, q=q, k_cache=k, v_cache=v, block_table=table,
                           seq_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype,
                           scale=1.0 / math.sqrt(head_dim), k_scale=ks, v_scale=vs,
@@ -291,7 +314,7 @@ def prefill_workload(*, seed: int, q_lens, ctx_lens, num_q_heads: int, num_kv_he
     cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(q_lens)
     q = _draw_q(rng, (int(cu[-1]), num_q_heads, head_dim), q_dtype)
-    k, v, ks, vs = _make_pools(rng, nb, num_kv_heads, head_dim, block_size, kv_dtype)
+    k, v, ks, vs = _make_pools(seed, nb, num_kv_heads, head_dim, block_size, kv_dtype)
     return PrefillWorkload(name=name, q=q, cu_q_lens=cu, k_cache=k, v_cache=v,
                            block_table=table, seq_lens=lens, q_dtype=q_dtype,
                            kv_dtype=kv_dtype, scale=1.0 / math.sqrt(head_dim),
@@ -347,7 +370,7 @@ def config4(pad: int = -1, partition_size: int = 512) -> MixedWorkload:
                                 -(-int(dec_lens.max()) // bs), pad)
     q_dec = _draw_q(rng, (16, hq, d), "bf16")
     q_pre = _draw_q(rng, (n_chunks * q_len, hq, d), "bf16")
-    k, v, _, _ = _make_pools(rng, nb, hkv, d, bs, "bf16")
+    k, v, _, _ = _make_pools(4, nb, hkv, d, bs, "bf16")
     scale = 1.0 / math.sqrt(d)
     dec = DecodeWorkload(name="C4-decode", q=q_dec, k_cache=k, v_cache=v, block_table=dtab,
                          seq_lens=dec_lens, q_dtype="bf16", kv_dtype="bf16", scale=scale,
