@@ -138,6 +138,19 @@ def decode_summary(wl, step_ms, kern_ms):
     }
 
 
+def copy_calibration():
+    """Three plain copies of 512 MiB: each reads and writes exactly 512 MiB."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "copies": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +159,13 @@ def main():
     ap.add_argument("--partition-size", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy three times (a known byte count "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the kernels run on one GPU's share; see DESIGN.md for how it would shard)",

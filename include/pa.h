@@ -18,7 +18,10 @@
  * Memory layouts (row-major, contiguous, all device memory):
  *   q, out (decode)    [num_seqs, num_q_heads, head_dim]
  *   q, out (prefill)   [total_q,  num_q_heads, head_dim]
- *   k_cache            [num_blocks, num_kv_heads, block_size, head_dim]  (token-major tiles)
+ *   k_cache            [num_blocks, num_kv_heads, head_dim / X, block_size, X], X the
+ *                      dims in 16 bytes (4 fp32, 8 bf16, 16 fp8): each (block, kv-head)
+ *                      tile is a run of 16-byte chunks of consecutive dims, with the
+ *                      token index inside each chunk
  *   v_cache            [num_blocks, num_kv_heads, head_dim, block_size]  (dim-major tiles)
  *   block_table        int32 [num_seqs, max_blocks_per_seq]; logical token t of
  *                      sequence b lives in physical block block_table[b][t / block_size]

@@ -27,7 +27,8 @@ this oracle writes out the plain definition of each step:
 * FP8 KV: value = e4m3fn(code) * scale[kv_head], per K and per V.
 
 Layouts (see ``k_block`` / ``v_block``, the only two places that know them):
-k_cache[num_blocks, Hkv, block_size, d], v_cache[num_blocks, Hkv, d, block_size].
+k_cache[num_blocks, Hkv, d/X, block_size, X] (X dims per chunk),
+v_cache[num_blocks, Hkv, d, block_size].
 Storage dtypes: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 codes.
 """
 from __future__ import annotations
@@ -61,8 +62,12 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 # the block-table walk
 # ---------------------------------------------------------------------------
 def k_block(k_cache, phys: int, h: int, n: int) -> np.ndarray:
-    """Keys of slots 0..n-1 of (physical block, kv-head): token-major K tile."""
-    return k_cache[phys, h, :n, :]
+    """Keys of slots 0..n-1 of (physical block, kv-head), as rows [n, d].
+
+    The K tile is stored as [d / X][block_size][X]: chunks of X consecutive
+    dims, the slot index inside a chunk (X is the array's last extent)."""
+    tile = k_cache[phys, h, :, :n, :]                  # [d/X, n, X]
+    return tile.transpose(1, 0, 2).reshape(n, -1)
 
 
 def v_block(v_cache, phys: int, h: int, n: int) -> np.ndarray:
@@ -80,8 +85,8 @@ def gather_kv(k_cache, v_cache, table_row, seq_len: int, h: int, kv_dtype: str,
     the last block.  Returns float64 K [L, d] and V [L, d] (fp8 values
     multiplied by the head's scale).
     """
-    bs = k_cache.shape[2]
-    d = k_cache.shape[3]
+    bs = v_cache.shape[3]
+    d = v_cache.shape[2]
     K = np.empty((seq_len, d), dtype=np.float64)
     V = np.empty((seq_len, d), dtype=np.float64)
     for j in range(-(-seq_len // bs)):

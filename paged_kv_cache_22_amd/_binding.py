@@ -41,10 +41,10 @@ class PAError(RuntimeError):
         super().__init__(f"{fn} failed: {status_string(status)}")
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_22_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m paged_kv_cache_22_amd.build`")
+    lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -105,10 +105,17 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_se
 
 
 def _kv_dims(q, k_cache, v_cache):
+    """Shapes of q [B, Hq, d], k_cache [NB, Hkv, d/X, bs, X] (X = dims per
+    16 bytes) and v_cache [NB, Hkv, d, bs]."""
     B, Hq, d = q.shape
-    NB, Hkv, bs, dk = k_cache.shape
-    if dk != d or tuple(v_cache.shape) != (NB, Hkv, d, bs):
-        raise ValueError("k_cache must be [NB, Hkv, bs, d] and v_cache [NB, Hkv, d, bs]")
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be [NB, Hkv, d/X, bs, X] with X = 16 bytes of dims")
+    NB, Hkv, nchunk, bs, x = k_cache.shape
+    if x * k_cache.element_size() != 16 or nchunk * x != d:
+        raise ValueError(f"k_cache chunks must hold 16 bytes ({16 // k_cache.element_size()} "
+                         f"dims) and cover head_dim {d}")
+    if tuple(v_cache.shape) != (NB, Hkv, d, bs):
+        raise ValueError("v_cache must be [NB, Hkv, d, bs]")
     return B, Hq, d, NB, Hkv, bs
 
 

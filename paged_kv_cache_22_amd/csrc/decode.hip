@@ -17,9 +17,13 @@
 //     row-swap permutes;
 //   * O^T[d x 16 heads] += V^T_blk . P^T on MFMA; the dim-major V tile makes
 //     V^T the A operand with each lane reading four consecutive tokens;
-//   * K/V of the next STAGES-1 blocks are in flight while a block is
-//     computed; block-table entries are fetched 64 at a time, one per lane,
-//     and broadcast with readlane, so no load waits on a table lookup.
+//   * a workgroup of 4 waves shares one (sequence, kv-head, partition): wave
+//     w takes blocks w, w+4, ...; the waves' softmax states are combined
+//     through LDS at the end;
+//   * K/V of the next block are in flight while a block is computed;
+//     block-table entries are fetched 64 at a time, one per lane, and
+//     broadcast with readlane, so no load waits on a table lookup; KV loads
+//     are non-temporal (each tile is read once).
 // Split-KV: partition p covers blocks [p*PB, (p+1)*PB); it writes its
 // normalised output and lse (natural log) for the log-sum-exp merge.
 #include "device.h"
@@ -29,14 +33,14 @@
 namespace pa {
 namespace {
 
-template <int D, int KIND, bool SPLIT, int STAGES>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
+template <int D, int KIND, bool SPLIT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
-    static_assert(64 % STAGES == 0, "STAGES must divide the 64-entry table window");
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;  // wave of the workgroup
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
@@ -49,8 +53,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     const int qh = h * G + r;
     const bool col_ok = r < G;
 
-    if (j0 >= nblk) {
-        if (!SPLIT && col_ok) {  // empty sequence: zeros
+    if (j0 >= nblk) {  // uniform over the workgroup
+        if (!SPLIT && w == 0 && col_ok) {  // empty sequence: zeros
             QT* o = reinterpret_cast<QT*>(a.out) + ((size_t)b * Hq + qh) * D;
 #pragma unroll
             for (int n = 0; n < NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
@@ -58,24 +62,27 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
         return;
     }
     const int j1 = min(nblk, j0 + pb);
+    // this wave takes blocks j0 + w, j0 + w + WAVES, ...: n_mine of them
+    const int n_mine = max(0, (j1 - j0 - w + WAVES - 1) / WAVES);
 
     typename T::QOp Q;
     T::load_q(Q, col_ok ? reinterpret_cast<const QT*>(a.q) + ((size_t)b * Hq + qh) * D : nullptr, c);
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;  // raw score -> base-2 logit (C > 0)
 
-    // block-table window: entries [tbase, tbase + 128), one per lane per half
-    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq;
-    int tbase = j0;
-    int tcur = (j0 + lane < j1) ? trow[j0 + lane] : 0;
-    int tnxt = (j0 + 64 + lane < j1) ? trow[j0 + 64 + lane] : 0;
+    // block-table window of this wave: lane i holds the entry of its block
+    // number tbase + i (and tbase + 64 + i in tnxt)
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0 + w;
+    int tbase = 0;
+    int tcur = (lane < n_mine) ? trow[lane * WAVES] : 0;
+    int tnxt = (64 + lane < n_mine) ? trow[(64 + lane) * WAVES] : 0;
 
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
     const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
 
-    auto issue = [&](typename T::Regs& R, int j) {
-        const int idx = j - tbase;
+    auto issue = [&](typename T::Regs& R, int i) {
+        const int idx = i - tbase;
         const int phys = idx < 64 ? __builtin_amdgcn_readlane(tcur, idx)
                                   : __builtin_amdgcn_readlane(tnxt, idx - 64);
         const size_t off = (size_t)phys * blk_stride;
@@ -87,50 +94,104 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = zero4();
 
-    typename T::Regs buf[STAGES];
+    // one block: scores, online softmax, PV
+    auto consume = [&](typename T::Regs& R, int ii) {
+        const int jj = j0 + w + ii * WAVES;  // logical block
+        // raw scores; the softmax scale (times log2 e, times the fp8 K scale)
+        // is applied to differences from the running max, so the maximum's
+        // weight is exactly exp2(0) = 1
+        const f32x4 sc = T::qk(R, Q);
+        float t[4] = {sc[0], sc[1], sc[2], sc[3]};
+        const int valid = L - jj * kBS;
+        if (valid < kBS) {  // tail block: mask tokens past L (scores and V)
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (j0 + s < j1) issue(buf[s], j0 + s);
+            for (int e = 0; e < 4; ++e)
+                if (4 * c + e >= valid) t[e] = -INFINITY;
+            T::mask_v(R, c, valid);
+        }
+        float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+        bm = group_max4(bm);
+        const float mn = fmaxf(m, bm);
+        if (__ballot(mn > m)) {  // some column's max moved: rescale
+            const float alpha = fast_exp2((m - mn) * C);
+            l *= alpha;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+            m = mn;
+        }
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - m) * C);
+        l += group_sum4((p[0] + p[1]) + (p[2] + p[3]));
+        T::pv(R, p, acc);
+    };
 
-    for (int j = j0; j < j1; j += STAGES) {
-        if (j - tbase >= 64) {  // slide the table window (uniform, once per 64 blocks)
+    // Two-stage software pipeline: block i+1 is in flight while block i is
+    // computed.  The steady-state loop issues its loads unconditionally and
+    // the tail is peeled, so the compiler's in-order load counting never
+    // waits for a prefetch before using older data, and no block is loaded
+    // twice.
+    if (n_mine > 0) {
+        typename T::Regs b0, b1;
+        issue(b0, 0);
+        int i = 0;
+        for (; i + 2 < n_mine; i += 2) {
+            if (i - tbase >= 64) {  // slide the table window (uniform, once per 64 blocks)
+                tbase += 64;
+                tcur = tnxt;
+                tnxt = (tbase + 64 + lane < n_mine) ? trow[(tbase + 64 + lane) * WAVES] : 0;
+            }
+            issue(b1, i + 1);
+            consume(b0, i);
+            issue(b0, i + 2);
+            consume(b1, i + 1);
+        }
+        if (i - tbase >= 64) {
             tbase += 64;
             tcur = tnxt;
-            tnxt = (tbase + 64 + lane < j1) ? trow[tbase + 64 + lane] : 0;
         }
+        if (i + 1 < n_mine) {
+            issue(b1, i + 1);
+            consume(b0, i);
+            consume(b1, i + 1);
+        } else {
+            consume(b0, i);
+        }
+    }
+
+    // combine the waves' partial softmax states through LDS (wave 0 finishes)
+    if constexpr (WAVES > 1) {
+        __shared__ float s_acc[WAVES - 1][NT * 4][64];
+        __shared__ float s_m[WAVES - 1][16], s_l[WAVES - 1][16];
+        if (w > 0) {
 #pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
-            const int jj = j + s;
-            if (jj < j1) {
-                if (jj + STAGES - 1 < j1) issue(buf[(s + STAGES - 1) % STAGES], jj + STAGES - 1);
-                typename T::Regs& R = buf[s];
-                // raw scores; the softmax scale (times log2 e, times the fp8 K
-                // scale) is applied to differences from the running max, so
-                // the maximum's weight is exactly exp2(0) = 1
-                const f32x4 sc = T::qk(R, Q);
-                float t[4] = {sc[0], sc[1], sc[2], sc[3]};
-                const int valid = L - jj * kBS;
-                if (valid < kBS) {  // tail block: mask tokens past L (scores and V)
+            for (int n = 0; n < NT; ++n)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * c + e >= valid) t[e] = -INFINITY;
-                    T::mask_v(R, c, valid);
-                }
-                float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-                bm = group_max4(bm);
-                const float mn = fmaxf(m, bm);
-                const float alpha = fast_exp2((m - mn) * C);
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - mn) * C);
-                const float ps = group_sum4((p[0] + p[1]) + (p[2] + p[3]));
-                l = l * alpha + ps;
-                m = mn;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-                T::pv(R, p, acc);
+                for (int e = 0; e < 4; ++e) s_acc[w - 1][n * 4 + e][lane] = acc[n][e];
+            if (c == 0) {
+                s_m[w - 1][r] = m;
+                s_l[w - 1][r] = l;
             }
         }
+        __syncthreads();
+        if (w > 0) return;
+        float M = m;
+#pragma unroll
+        for (int v = 0; v < WAVES - 1; ++v) M = fmaxf(M, s_m[v][r]);
+        const float f0 = fast_exp2((m - M) * C);  // wave 0 always has a block: M finite
+        l *= f0;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] *= f0;
+#pragma unroll
+        for (int v = 0; v < WAVES - 1; ++v) {
+            const float f = fast_exp2((s_m[v][r] - M) * C);  // 0 for a wave without blocks
+            l += f * s_l[v][r];
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[n][e] += f * s_acc[v][n * 4 + e][lane];
+        }
+        m = M;
     }
 
     if (!col_ok) return;
@@ -153,12 +214,16 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     }
 }
 
-template <int KIND> constexpr int stages_for() { return KIND == KV_FP8 ? 4 : 2; }
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;
 
 template <int D, int KIND, bool SPLIT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), SPLIT ? (unsigned)a.grid_parts : 1u);
-    hipLaunchKernelGGL((decode_kernel<D, KIND, SPLIT, stages_for<KIND>()>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, KIND, SPLIT, kWaves>), grid,
+                       dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 

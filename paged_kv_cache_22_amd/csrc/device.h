@@ -120,4 +120,31 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ unsigned ld4(const void* p) { return *reinterpret_cast<const unsigned*>(p); }
 
+// loads of KV data, which every kernel reads exactly once: non-temporal, so
+// the stream of K/V tiles does not evict what is reused (tables, q, partials)
+#ifndef PA_KV_NONTEMPORAL
+#define PA_KV_NONTEMPORAL 1
+#endif
+__device__ __forceinline__ u32x4 ldkv16(const void* p) {
+#if PA_KV_NONTEMPORAL
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return ld16(p);
+#endif
+}
+__device__ __forceinline__ u32x2 ldkv8(const void* p) {
+#if PA_KV_NONTEMPORAL
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#else
+    return ld8(p);
+#endif
+}
+__device__ __forceinline__ unsigned ldkv4(const void* p) {
+#if PA_KV_NONTEMPORAL
+    return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+#else
+    return ld4(p);
+#endif
+}
+
 }  // namespace pa

@@ -22,12 +22,11 @@
 namespace pa {
 namespace {
 
-template <int D, int KIND, int NC, int STAGES>
+template <int D, int KIND, int NC>
 __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
-    static_assert(64 % STAGES == 0, "STAGES must divide the 64-entry table window");
 
     const int lane = threadIdx.x;
     const int r = lane & 15, c = lane >> 4;
@@ -71,8 +70,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
     const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
-    auto issue = [&](typename T::Regs& R, int j) {
-        const int idx = j - tbase;
+    auto issue = [&](typename T::Regs& R, int jb) {
+        const int idx = jb - tbase;
         const int phys = idx < 64 ? __builtin_amdgcn_readlane(tcur, idx)
                                   : __builtin_amdgcn_readlane(tnxt, idx - 64);
         const size_t off = (size_t)phys * blk_stride;
@@ -89,51 +88,63 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
         for (int n = 0; n < NT; ++n) acc[ct][n] = zero4();
     }
 
-    typename T::Regs buf[STAGES];
+    // one key block against every column tile of the wave
+    auto consume = [&](typename T::Regs& R, int jj) {
+        const int valid = L - jj * kBS;
+        if (valid < kBS) T::mask_v(R, c, valid);  // cache slots past L
+        const bool diag = jj >= full_end;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nblk) issue(buf[s], s);
+        for (int ct = 0; ct < NC; ++ct) {
+            const f32x4 sc = T::qk(R, Q[ct]);   // raw scores, as in decode
+            float t[4] = {sc[0], sc[1], sc[2], sc[3]};
+            if (diag) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (jj * kBS + 4 * c + e > pos[ct]) t[e] = -INFINITY;
+            }
+            float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+            bm = group_max4(bm);
+            const float mn = fmaxf(m[ct], bm);
+            if (__ballot(mn > m[ct])) {
+                const float alpha = fast_exp2((m[ct] - mn) * C);
+                l[ct] *= alpha;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+                m[ct] = mn;
+            }
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - m[ct]) * C);
+            l[ct] += group_sum4((p[0] + p[1]) + (p[2] + p[3]));
+            T::pv(R, p, acc[ct]);
+        }
+    };
 
-    for (int j = 0; j < nblk; j += STAGES) {
+    // two-stage pipeline with a peeled tail, as in decode
+    typename T::Regs b0, b1;
+    issue(b0, 0);
+    int j = 0;
+    for (; j + 2 < nblk; j += 2) {
         if (j - tbase >= 64) {
             tbase += 64;
             tcur = tnxt;
             tnxt = (tbase + 64 + lane < nblk) ? trow[tbase + 64 + lane] : 0;
         }
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
-            const int jj = j + s;
-            if (jj < nblk) {
-                if (jj + STAGES - 1 < nblk) issue(buf[(s + STAGES - 1) % STAGES], jj + STAGES - 1);
-                typename T::Regs& R = buf[s];
-                const int valid = L - jj * kBS;
-                if (valid < kBS) T::mask_v(R, c, valid);  // cache slots past L
-                const bool diag = jj >= full_end;
-#pragma unroll
-                for (int ct = 0; ct < NC; ++ct) {
-                    const f32x4 sc = T::qk(R, Q[ct]);   // raw scores, as in decode
-                    float t[4] = {sc[0], sc[1], sc[2], sc[3]};
-                    if (diag) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jj * kBS + 4 * c + e > pos[ct]) t[e] = -INFINITY;
-                    }
-                    float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-                    bm = group_max4(bm);
-                    const float mn = fmaxf(m[ct], bm);
-                    const float alpha = fast_exp2((m[ct] - mn) * C);
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - mn) * C);
-                    const float ps = group_sum4((p[0] + p[1]) + (p[2] + p[3]));
-                    l[ct] = l[ct] * alpha + ps;
-                    m[ct] = mn;
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
-                    T::pv(R, p, acc[ct]);
-                }
-            }
-        }
+        issue(b1, j + 1);
+        consume(b0, j);
+        issue(b0, j + 2);
+        consume(b1, j + 1);
+    }
+    if (j - tbase >= 64) {
+        tbase += 64;
+        tcur = tnxt;
+    }
+    if (j + 1 < nblk) {
+        issue(b1, j + 1);
+        consume(b0, j);
+        consume(b1, j + 1);
+    } else {
+        consume(b0, j);
     }
 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
@@ -157,7 +168,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const long rows = (long)a.max_q_len * G;
     dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + 16 * kNC - 1) / (16 * kNC)));
-    hipLaunchKernelGGL((prefill_kernel<D, KIND, kNC, 2>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, KIND, kNC>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,11 +1,15 @@
 // Per-KV-dtype access to one (block, kv-head) tile of the paged cache, in the
 // MFMA operand layouts the attention kernels use.  gfx950 / CDNA4.
 //
-// A K tile is [16 tokens][D] (token-major), a V tile is [D][16 tokens]
-// (dim-major), so that both products of attention read their operands as
-// contiguous runs: the score product S^T = K . Q^T contracts over dims, which
-// run along a K row, and the output product O^T = V^T . P^T contracts over
-// tokens, which run along a V row.
+// A K tile is [D*eb/16 chunks][16 tokens][16 bytes]: 16-byte chunks of
+// consecutive dims with the token index inside each chunk.  A V tile is
+// [D][16 tokens] (dim-major).  Both products of attention then read their
+// MFMA operands as whole contiguous runs: for the score product
+// S^T = K . Q^T (contraction over dims) lane (r, c) takes chunk 4i + c of
+// token r, so one load instruction of the wave reads 1 KiB in one piece; for
+// the output product O^T = V^T . P^T (contraction over tokens) lane (r, c)
+// takes tokens 4c..4c+3 of dim 16n + r, so one instruction reads 16 whole
+// dim rows.
 #pragma once
 
 #include "device.h"
@@ -39,9 +43,9 @@ template <int D> struct Tile<KV_BF16, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * (D * 2) + (4 * i + c) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld8(vt + (16 * n + r) * (kBS * 2) + c * 8);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (kBS * 2) + c * 8);
     }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();
@@ -83,9 +87,9 @@ template <int D> struct Tile<KV_FP8, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * D + (4 * i + c) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld4(vt + (16 * n + r) * kBS + c * 4);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * kBS + c * 4);
     }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();
@@ -130,9 +134,9 @@ template <int D> struct Tile<KV_F32, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + r * (D * 4) + (4 * i + c) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld16(vt + (16 * n + r) * (kBS * 4) + c * 16);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (kBS * 4) + c * 16);
     }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();

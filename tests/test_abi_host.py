@@ -118,7 +118,7 @@ def test_prefill_rejects():
 
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(2, 8, 64)
-    k = torch.zeros(4, 2, 16, 64)
+    k = torch.zeros(4, 2, 16, 16, 4)
     v = torch.zeros(4, 2, 64, 16)
     bt = torch.zeros(2, 2, dtype=torch.int32)
     sl = torch.ones(2, dtype=torch.int32)

@@ -167,7 +167,7 @@ def _exact_selection_sweep(wl, partitions):
     for k in range(nblk_max):
         taus = [min(16 * k + (b * 7) % 16, int(L) - 1) for b, L in enumerate(wl.seq_lens)]
         for b, t in enumerate(taus):
-            d.k[int(wl.block_table[b, t // 16]), :, t % 16, :] = one
+            d.k[int(wl.block_table[b, t // 16]), :, :, t % 16, :] = one
         for P in partitions:
             got = f64(run_decode(d, partition_size=P))
             for b, t in enumerate(taus):
@@ -178,7 +178,7 @@ def _exact_selection_sweep(wl, partitions):
                         raise AssertionError(f"block {k} seq {b} tau {t} head {j} P={P}")
                     checked += 1
         for b, t in enumerate(taus):
-            d.k[int(wl.block_table[b, t // 16]), :, t % 16, :] = minus
+            d.k[int(wl.block_table[b, t // 16]), :, :, t % 16, :] = minus
     assert d_head == 128 and checked > 0
     return checked
 
@@ -203,14 +203,14 @@ def test_exact_selection_c3_partitions():
     for p in range(-(-wl.max_seq_len // 512)):
         taus = [min(512 * p + 301, int(L) - 1) for L in wl.seq_lens]
         for b, t in enumerate(taus):
-            d.k[int(wl.block_table[b, t // 16]), :, t % 16, :] = one
+            d.k[int(wl.block_table[b, t // 16]), :, :, t % 16, :] = one
         got = run_decode(d, partition_size=512)
         for b, t in enumerate(taus):
             phys = int(wl.block_table[b, t // 16])
             want = vals_all[phys, :, :, t % 16].repeat_interleave(4, dim=0)
             assert torch.equal(got[b], want), (p, b, t)
         for b, t in enumerate(taus):
-            d.k[int(wl.block_table[b, t // 16]), :, t % 16, :] = minus
+            d.k[int(wl.block_table[b, t // 16]), :, :, t % 16, :] = minus
 
 
 def _poisoned(wl):
@@ -223,13 +223,13 @@ def _poisoned(wl):
         if L % 16:
             phys = int(wl.block_table[b, L // 16])
             if wl.kv_dtype == "bf16":
-                k[phys, :, L % 16:, :] = nan
+                k[phys, :, :, L % 16:, :] = nan
                 v[phys, :, :, L % 16:] = nan
             elif wl.kv_dtype == "fp8":
-                k[phys, :, L % 16:, :] = 0x7F
+                k[phys, :, :, L % 16:, :] = 0x7F
                 v[phys, :, :, L % 16:] = 0x7F
             else:
-                k[phys, :, L % 16:, :] = np.nan
+                k[phys, :, :, L % 16:, :] = np.nan
                 v[phys, :, :, L % 16:] = np.nan
     return k, v
 

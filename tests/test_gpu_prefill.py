@@ -77,7 +77,7 @@ def test_causal_boundary_exact_selection():
     for tau in (0, 15, 16, 39, 40, 41, 63, 64, 89):
         k = -np.ones(wl.k_cache.shape, np.float32)
         phys = int(wl.block_table[0, tau // 16])
-        k[phys, :, tau % 16, :] = 1.0
+        k[phys, :, :, tau % 16, :] = 1.0
         wl.k_cache[:] = W.to_bf16_bits(k)
         got = f64(run_prefill(Dev(wl)))
         for i in range(n):

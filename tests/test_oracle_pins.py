@@ -32,16 +32,19 @@ FACTS = json.load(open(GOLD))
 # ---------------------------------------------------------------------------
 # helpers that build a paged cache from contiguous K/V (test-side scatter)
 # ---------------------------------------------------------------------------
-def scatter_to_pages(Ks, Vs, bs, rng, extra_blocks=3, fill=np.nan):
+def scatter_to_pages(Ks, Vs, bs, rng, extra_blocks=3, fill=np.nan, x=None):
     """Ks[b]: [L_b, Hkv, d] float64.  Returns pools, table, lens with a random
-    physical placement; unused slots hold ``fill``."""
+    physical placement; unused slots hold ``fill``.  K chunks hold x dims
+    (4 when d allows, else d)."""
     B = len(Ks)
     Hkv, d = Ks[0].shape[1], Ks[0].shape[2]
+    if x is None:
+        x = 4 if d % 4 == 0 else d
     lens = np.array([k.shape[0] for k in Ks], dtype=np.int32)
     nblk = [-(-int(L) // bs) for L in lens]
     nb = sum(nblk) + extra_blocks
     perm = rng.permutation(nb)
-    kp = np.full((nb, Hkv, bs, d), fill)
+    kp = np.full((nb, Hkv, d // x, bs, x), fill)
     vp = np.full((nb, Hkv, d, bs), fill)
     table = np.full((B, max(max(nblk), 1)), -1, dtype=np.int32)
     pos = 0
@@ -52,7 +55,7 @@ def scatter_to_pages(Ks, Vs, bs, rng, extra_blocks=3, fill=np.nan):
             for slot in range(bs):
                 t = jb * bs + slot
                 if t < lens[b]:
-                    kp[phys, :, slot, :] = Ks[b][t]
+                    kp[phys, :, :, slot, :] = Ks[b][t].reshape(Hkv, d // x, x)
                     vp[phys, :, :, slot] = Vs[b][t]
     return kp, vp, table, lens
 
@@ -213,8 +216,8 @@ def test_prefill_without_context_is_plain_causal():
 def test_worked_example_two_tokens():
     """q = (1, 0), keys (1, 0) and (0, 0), values e1 and e2, scale 1:
     scores (1, 0) -> weights e/(1+e), 1/(1+e); lse = ln(1 + e)."""
-    kp = np.zeros((1, 1, 16, 2), np.float32); vp = np.zeros((1, 1, 2, 16), np.float32)
-    kp[0, 0, 0] = [1, 0]; kp[0, 0, 1] = [0, 0]
+    kp = np.zeros((1, 1, 1, 16, 2), np.float32); vp = np.zeros((1, 1, 2, 16), np.float32)
+    kp[0, 0, 0, 0] = [1, 0]; kp[0, 0, 0, 1] = [0, 0]
     vp[0, 0, :, 0] = [1, 0]; vp[0, 0, :, 1] = [0, 1]
     q = np.array([[[1.0, 0.0]]], np.float32)
     out, lse = oracle.decode(q, kp, vp, np.zeros((1, 1), np.int32), np.array([2], np.int32),
@@ -266,7 +269,7 @@ def test_one_token_returns_v0_exactly():
 
 
 def test_zero_length_sequence():
-    kp = np.zeros((2, 1, 16, 4), np.float32); vp = np.zeros((2, 1, 4, 16), np.float32)
+    kp = np.zeros((2, 1, 1, 16, 4), np.float32); vp = np.zeros((2, 1, 4, 16), np.float32)
     q = np.ones((1, 2, 4), np.float32)
     out, lse = oracle.decode(q, kp, vp, np.full((1, 1), -1, np.int32), np.array([0], np.int32),
                              0.5, "f32", "f32")
@@ -391,7 +394,7 @@ def test_exact_selection_decode_and_causal_boundary():
 # ---------------------------------------------------------------------------
 def test_config_shapes_and_tables():
     c1 = W.config1()
-    assert c1.q.shape == (4, 8, 64) and c1.k_cache.shape == (64, 2, 16, 64)
+    assert c1.q.shape == (4, 8, 64) and c1.k_cache.shape == (64, 2, 16, 16, 4)
     assert c1.v_cache.shape == (64, 2, 64, 16)
     assert (c1.seq_lens >= 1).all() and (c1.seq_lens <= 200).all()
     used = np.concatenate([c1.block_table[b, :-(-int(L) // 16)] for b, L in enumerate(c1.seq_lens)])

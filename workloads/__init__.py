@@ -14,7 +14,9 @@ Storage conventions (raw bits, so that each consumer widens them itself):
 
 Cache layout (one contiguous tile per (block, kv-head)):
 
-* ``k_cache[num_blocks, num_kv_heads, block_size, head_dim]``  token-major
+* ``k_cache[num_blocks, num_kv_heads, head_dim/X, block_size, X]`` with X the
+  dims in 16 bytes (4 fp32, 8 bf16, 16 fp8): 16-byte chunks of consecutive
+  dims, the token index inside each chunk
 * ``v_cache[num_blocks, num_kv_heads, head_dim, block_size]``  dim-major
 
 The pages name block tables and sequence lengths as the metadata of the paged
@@ -85,6 +87,11 @@ def to_fp8_codes(x: np.ndarray, scale: np.ndarray, axis_scale: int) -> np.ndarra
     return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
+def chunk_dims(kv_dtype: str) -> int:
+    """Dims per 16-byte chunk of the K tile layout."""
+    return {"f32": 4, "bf16": 8, "fp8": 16}[kv_dtype]
+
+
 def kv_bytes_per_token(num_kv_heads: int, head_dim: int, kv_bytes: float,
                        num_layers: int = 1) -> float:
     """K plus V bytes one token occupies: 2 * layers * kv-heads * d * bytes.
@@ -103,7 +110,7 @@ class DecodeWorkload:
     """One decode query per sequence over a paged KV cache."""
     name: str
     q: np.ndarray                 # [B, Hq, d]   f32 / bf16 bits
-    k_cache: np.ndarray           # [NB, Hkv, bs, d]
+    k_cache: np.ndarray           # [NB, Hkv, d/X, bs, X]
     v_cache: np.ndarray           # [NB, Hkv, d, bs]
     block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
     seq_lens: np.ndarray          # int32 [B]
@@ -123,7 +130,7 @@ class DecodeWorkload:
     @property
     def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
     @property
-    def block_size(self) -> int: return int(self.k_cache.shape[2])
+    def block_size(self) -> int: return int(self.v_cache.shape[3])
     @property
     def num_blocks(self) -> int: return int(self.k_cache.shape[0])
     @property
@@ -169,7 +176,7 @@ class PrefillWorkload:
     @property
     def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
     @property
-    def block_size(self) -> int: return int(self.k_cache.shape[2])
+    def block_size(self) -> int: return int(self.v_cache.shape[3])
     @property
     def num_blocks(self) -> int: return int(self.k_cache.shape[0])
     @property
@@ -259,7 +266,8 @@ def _tables_from_perm(perm, lens, block_size, max_blocks, pad):
 def _make_pools(seed, nb, hkv, d, bs, kv_dtype):
     k = _draw_pool(seed, 1, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
     v = _draw_pool(seed, 2, nb, hkv, d, bs, "f32" if kv_dtype == "fp8" else kv_dtype)
-    k = k.reshape(nb, hkv, bs, d)
+    x = chunk_dims(kv_dtype)
+    k = k.reshape(nb, hkv, d // x, bs, x)
     v = v.reshape(nb, hkv, d, bs)
     ks = vs = None
     if kv_dtype == "fp8":
