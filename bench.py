@@ -5,8 +5,9 @@ Headline: KV GB/s (and % of the 8 TB/s HBM peak) plus tokens-attended/s of
 bf16 decode at the Llama-3-8B layer shape: 64 sequences, 32 q-heads / 8
 kv-heads, head_dim 128, block_size 16, lengths uniform in [512, 4096] (seed
 2), block tables a random permutation of one pool.  A step is one pass of
-the decode path over that batch: the split-KV partition kernel plus the
-log-sum-exp merge (pa_decode's two launches), inputs resident in HBM.  Before
+the decode path over that batch: pa_decode (the split-KV partition kernel,
+then the log-sum-exp merge for sequences with several partitions), inputs
+resident in HBM.  Before
 every timed step a 1 GiB buffer is rewritten so no KV survives in the 256 MB
 Infinity Cache; step times come from HIP events on the launch stream.
 
@@ -59,39 +60,31 @@ class Timer:
 
 
 def time_decode(torch, pa, d, wl, P, steps, warmup, flush):
-    """Returns (per-step ms list, per-step partition-kernel ms list)."""
-    B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
+    """Per-step ms of pa_decode (the partition kernel, then the merge kernel
+    for sequences split into several partitions)."""
     out = torch.empty_like(d.q)
-    if P > 0:
-        pmax = -(-wl.max_seq_len // P)
-        po = torch.empty((B, Hq, pmax, D), dtype=torch.float32, device="cuda")
-        pl = torch.empty((B, Hq, pmax), dtype=torch.float32, device="cuda")
+    ws_bytes = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                        wl.max_seq_len, P)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     def launch(ev):
         ev[0].record()
-        if P > 0:
-            pa.decode_partitions(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
-                                 partition_size=P, scale=wl.scale, k_scale=d.ks, v_scale=d.vs,
-                                 partial_out=po, partial_lse=pl)
-            ev[1].record()
-            pa.merge_partitions(po, pl, d.sl, partition_size=P, out=out)
-        else:
-            pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
-                      partition_size=0, k_scale=d.ks, v_scale=d.vs, out=out)
-            ev[1].record()
-        ev[2].record()
+        pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                  partition_size=P, k_scale=d.ks, v_scale=d.vs, out=out, workspace=ws)
+        ev[1].record()
 
-    wt = Timer(torch, warmup, 3)
+    wt = Timer(torch, warmup, 2)
     for i in range(warmup):
         flush.add_(1)
         launch(wt.ev[i])
     torch.cuda.synchronize()
-    t = Timer(torch, steps, 3)
+    t = Timer(torch, steps, 2)
     for i in range(steps):
         flush.add_(1)
         launch(t.ev[i])
     torch.cuda.synchronize()
-    return [t.ms(i, 0, 2) for i in range(steps)], [t.ms(i, 0, 1) for i in range(steps)]
+    ms = [t.ms(i, 0, 1) for i in range(steps)]
+    return ms, ms
 
 
 def time_prefill(torch, pa, d, wl, steps, warmup, flush):
@@ -156,7 +149,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -102,7 +102,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * directly.  partition_size > 0 (a multiple of block_size): split-KV; each
  * partition p covers tokens [p*P, min((p+1)*P, L)) and writes its normalised
  * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
- * pa_merge_partitions) writes out.  max_seq_len is the caller's host-side
+ * pa_merge_partitions) writes out.  A sequence that fits in one partition
+ * is written directly by the partition kernel (bit-identical to merging its
+ * single partition).  A workspace serves one call at a time.
+ * max_seq_len is the caller's host-side
  * bound on seq_lens; it sizes the grid.  A sequence of length 0 gets zeros.
  * scale is the softmax scale (1/sqrt(head_dim) for plain attention); it
  * must be finite and > 0 (PA_ERR_SHAPE otherwise), and so must every fp8

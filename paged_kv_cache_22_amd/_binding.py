@@ -122,7 +122,9 @@ def _kv_dims(q, k_cache, v_cache):
 def decode(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
            scale: Optional[float] = None, partition_size: int = 0, k_scale=None, v_scale=None,
            out=None, workspace=None):
-    """Decode attention (pa_decode).  Returns ``out`` [B, Hq, d] in q's dtype."""
+    """Decode attention (pa_decode).  Returns ``out`` [B, Hq, d] in q's dtype.
+    ``workspace`` (uint8, at least decode_workspace_size bytes) is allocated
+    here when None."""
     torch = _torch()
     B, Hq, d, NB, Hkv, bs = _kv_dims(q, k_cache, v_cache)
     if out is None:

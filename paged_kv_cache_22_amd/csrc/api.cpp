@@ -213,31 +213,38 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
     if (num_seqs == 0) return PA_OK;
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
-    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
-    float* part_out = reinterpret_cast<float*>(workspace);
-    float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                               round_up(rows * head_dim * sizeof(float), kRegionAlign));
-    if (parts > 0) {
-        a.part_out = part_out;
-        a.part_lse = part_lse;
-        a.max_parts = parts;
-        a.partition_blocks = partition_size / block_size;
-        a.grid_parts = parts;
-        st = hip_status(pa::launch_decode(a, stream));
-        if (st != PA_OK) return st;
+    if (parts == 0) {  // every sequence is empty: the one-pass kernel writes the zeros
+        a.out = out;
+        a.partition_blocks = 0;
+        a.grid_parts = 1;
+        return hip_status(pa::launch_decode(a, stream));
     }
+    // workspace: partial outputs | partial lse
+    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    char* ws = reinterpret_cast<char*>(workspace);
+    const size_t off_lse = round_up(rows * head_dim * sizeof(float), kRegionAlign);
+    a.out = out;
+    a.part_out = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + off_lse);
+    a.single_direct = 1;
+    a.max_parts = parts;
+    a.partition_blocks = partition_size / block_size;
+    a.grid_parts = parts;
+    st = hip_status(pa::launch_decode(a, stream));
+    if (st != PA_OK) return st;
     pa::MergeArgs m{};
     m.out = out;
     m.out_dtype = q_dtype;
     m.out_lse = nullptr;
-    m.part_out = part_out;
-    m.part_lse = part_lse;
+    m.part_out = a.part_out;
+    m.part_lse = a.part_lse;
     m.seq_lens = seq_lens;
     m.partition_size = partition_size;
     m.max_parts = parts;
     m.num_seqs = num_seqs;
     m.num_q_heads = num_q_heads;
     m.head_dim = head_dim;
+    m.skip_single = 1;
     return hip_status(pa::launch_merge(m, stream));
 }
 

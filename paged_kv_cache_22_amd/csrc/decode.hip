@@ -159,59 +159,66 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
         }
     }
 
-    // combine the waves' partial softmax states through LDS (wave 0 finishes)
+    // ---- combine the waves' softmax states through LDS (wave 0 holds the result)
+    constexpr int kCombineFloats = (WAVES - 1) * (NT * 4 * 64 + 32);
+    __shared__ float smem[kCombineFloats > 1 ? kCombineFloats : 1];
     if constexpr (WAVES > 1) {
-        __shared__ float s_acc[WAVES - 1][NT * 4][64];
-        __shared__ float s_m[WAVES - 1][16], s_l[WAVES - 1][16];
+        float* s_acc = smem;                                  // [WAVES-1][NT*4][64]
+        float* s_m = smem + (WAVES - 1) * NT * 4 * 64;       // [WAVES-1][16]
+        float* s_l = s_m + (WAVES - 1) * 16;                 // [WAVES-1][16]
         if (w > 0) {
 #pragma unroll
             for (int n = 0; n < NT; ++n)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s_acc[w - 1][n * 4 + e][lane] = acc[n][e];
+                for (int e = 0; e < 4; ++e) s_acc[((w - 1) * NT * 4 + n * 4 + e) * 64 + lane] = acc[n][e];
             if (c == 0) {
-                s_m[w - 1][r] = m;
-                s_l[w - 1][r] = l;
+                s_m[(w - 1) * 16 + r] = m;
+                s_l[(w - 1) * 16 + r] = l;
             }
         }
         __syncthreads();
-        if (w > 0) return;
-        float M = m;
+        if (w == 0) {
+            float M = m;
 #pragma unroll
-        for (int v = 0; v < WAVES - 1; ++v) M = fmaxf(M, s_m[v][r]);
-        const float f0 = fast_exp2((m - M) * C);  // wave 0 always has a block: M finite
-        l *= f0;
+            for (int v = 0; v < WAVES - 1; ++v) M = fmaxf(M, s_m[v * 16 + r]);
+            const float f0 = fast_exp2((m - M) * C);  // wave 0 always has a block: M finite
+            l *= f0;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] *= f0;
+            for (int n = 0; n < NT; ++n) acc[n] *= f0;
 #pragma unroll
-        for (int v = 0; v < WAVES - 1; ++v) {
-            const float f = fast_exp2((s_m[v][r] - M) * C);  // 0 for a wave without blocks
-            l += f * s_l[v][r];
+            for (int v = 0; v < WAVES - 1; ++v) {
+                const float f = fast_exp2((s_m[v * 16 + r] - M) * C);  // 0 for a wave without blocks
+                l += f * s_l[v * 16 + r];
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
+                for (int n = 0; n < NT; ++n)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[n][e] += f * s_acc[v][n * 4 + e][lane];
+                    for (int e = 0; e < 4; ++e) acc[n][e] += f * s_acc[(v * NT * 4 + n * 4 + e) * 64 + lane];
+            }
+            m = M;
         }
-        m = M;
     }
 
-    if (!col_ok) return;
+    if (w > 0 || !col_ok) return;
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
     const float inv = vscale / l;
-    if constexpr (SPLIT) {
-        const size_t row = (size_t)b * Hq + qh;
-        float* po = a.part_out + (row * a.max_parts + part) * D;
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-            store4(po + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv,
-                   acc[n][3] * inv);
-        if (c == 0) a.part_lse[row * a.max_parts + part] = (m * C + fast_log2(l)) * kLn2;
-    } else {
+    // the one-pass mode, and a split sequence with a single partition when
+    // asked to, write the output here
+    const int np = (nblk + pb - 1) / pb;
+    if (!SPLIT || (np == 1 && a.single_direct)) {
         QT* o = reinterpret_cast<QT*>(a.out) + ((size_t)b * Hq + qh) * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
             store4(o + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv,
                    acc[n][3] * inv);
+        return;
     }
+    const size_t row = (size_t)b * Hq + qh;
+    float* po = a.part_out + (row * a.max_parts + part) * D;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+        store4(po + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv,
+               acc[n][3] * inv);
+    if (c == 0) a.part_lse[row * a.max_parts + part] = (m * C + fast_log2(l)) * kLn2;
 }
 
 #ifndef PA_DECODE_WAVES

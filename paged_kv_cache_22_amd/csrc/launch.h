@@ -12,6 +12,8 @@ struct DecodeArgs {
     void* out;            // [B, Hq, D] in q's dtype (one-pass mode)
     float* part_out;      // [B, Hq, max_parts, D]     (split mode)
     float* part_lse;      // [B, Hq, max_parts]
+    int single_direct;    // split mode: a sequence with one partition writes `out`
+                          // directly instead of a partial (the merge then skips it)
     int max_parts;
     const void* q;
     const void* k_cache;
@@ -38,6 +40,7 @@ struct MergeArgs {
     const int32_t* seq_lens;
     int partition_size, max_parts;
     int num_seqs, num_q_heads, head_dim;
+    int skip_single;      // leave sequences with exactly one partition untouched
 };
 
 struct PrefillArgs {

@@ -25,6 +25,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     const size_t row = (size_t)b * Hq + qh;
     const int L = a.seq_lens[b];
     const int np = min((L + a.partition_size - 1) / a.partition_size, a.max_parts);
+    if (a.skip_single && np == 1) return;  // written by the partition kernel
     const float* lse = a.part_lse + row * a.max_parts;
     const float* po = a.part_out + row * a.max_parts * D + lane * V;
 

@@ -281,9 +281,14 @@ def test_batch_invariance_bit_identical():
 
 
 def test_split_equals_partitions_then_merge_bitwise():
+    """pa_decode (split) is pa_decode_partitions followed by the merge kernel,
+    bit for bit, including sequences short enough for a single partition
+    (written directly by the partition kernel); the partition kernel's own
+    results match the oracle's partials."""
     import paged_kv_cache_22_amd as pa
     wl = W.decode_workload(seed=130, num_seqs=7, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                           len_lo=1, len_hi=5000, q_dtype="bf16", kv_dtype="bf16")
+                           len_lo=1, len_hi=5000, q_dtype="bf16", kv_dtype="bf16",
+                           seq_lens=[5000, 1, 512, 513, 3000, 100, 1024])
     d = Dev(wl)
     P = 512
     out = run_decode(d, partition_size=P)
@@ -292,7 +297,6 @@ def test_split_equals_partitions_then_merge_bitwise():
     out2 = pa.merge_partitions(po, pl, d.sl, partition_size=P, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
-    # the partition kernel's own results against the oracle's partials
     pmax = po.shape[2]
     ref_o, ref_l = oracle.decode_partials(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
                                           wl.seq_lens, wl.scale, "bf16", "bf16", P, pmax)
@@ -301,6 +305,22 @@ def test_split_equals_partitions_then_merge_bitwise():
     valid = np.broadcast_to(valid, ref_l.shape)
     compare(f64(po)[valid], ref_o[valid], "bf16", "partition outputs")
     assert np.abs(f64(pl)[valid] - ref_l[valid]).max() < 1e-3
+
+
+def test_workspace_reuse_is_deterministic():
+    import paged_kv_cache_22_amd as pa
+    wl = W.decode_workload(seed=131, num_seqs=9, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=1, len_hi=3000, q_dtype="bf16", kv_dtype="bf16")
+    d = Dev(wl)
+    P = 256
+    n = pa.decode_workspace_size(wl.num_seqs, 32, 128, wl.max_seq_len, P)
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")   # stale contents are fine
+    outs = [pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                      partition_size=P, workspace=ws).clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    compare(f64(outs[0]), oracle_decode(wl)[0], "bf16", "workspace reuse")
 
 
 def test_merge_on_oracle_partials():
