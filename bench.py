@@ -31,6 +31,36 @@ METRIC = "paged-attn decode KV GB/s (% HBM peak) + tokens-attended/s, Llama-3-8B
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 FLUSH_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_PROFILE = os.path.join(PROFILES, "decode_kernel_bf16_llama3_8b_c2_traffic.txt")
+KERNEL_SOURCES = ["decode.hip", "tiles.h", "device.h"]
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the decode kernel (so a stored counter
+    reading is used only for the kernel it was taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_22_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(partition_size):
+    """HBM bytes per launch of the decode kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if that summary was
+    taken on other kernel sources or another partition size."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_PROFILE) if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    if int(kv.get("partition_size", -1)) != partition_size:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl):
@@ -85,6 +115,33 @@ def time_decode(torch, pa, d, wl, P, steps, warmup, flush):
     torch.cuda.synchronize()
     ms = [t.ms(i, 0, 1) for i in range(steps)]
     return ms, ms
+
+
+def time_partition_kernel(torch, pa, d, wl, P, steps, warmup, flush):
+    """Per-launch ms of the split-KV partition kernel alone (pa_decode_partitions),
+    HIP events on the launch stream."""
+    pmax = -(-wl.max_seq_len // P)
+    po = torch.empty((wl.num_seqs, wl.num_q_heads, pmax, wl.head_dim), dtype=torch.float32,
+                     device="cuda")
+    pl = torch.empty((wl.num_seqs, wl.num_q_heads, pmax), dtype=torch.float32, device="cuda")
+
+    def launch(ev):
+        ev[0].record()
+        pa.decode_partitions(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                             partition_size=P, scale=wl.scale, k_scale=d.ks, v_scale=d.vs,
+                             partial_out=po, partial_lse=pl)
+        ev[1].record()
+
+    for i in range(warmup):
+        flush.add_(1)
+        launch(Timer(torch, 1, 2).ev[0])
+    torch.cuda.synchronize()
+    t = Timer(torch, steps, 2)
+    for i in range(steps):
+        flush.add_(1)
+        launch(t.ev[i])
+    torch.cuda.synchronize()
+    return [t.ms(i, 0, 1) for i in range(steps)]
 
 
 def time_prefill(torch, pa, d, wl, steps, warmup, flush):
@@ -144,6 +201,32 @@ def copy_calibration():
                       "copies": 3}))
 
 
+def profile_one(args, W):
+    """Time one non-headline workload alone (for per-kernel profiling)."""
+    import torch
+    import paged_kv_cache_22_amd as pa
+    from workloads.device import Dev
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    n = int(args.workload[1])
+    res = {"workload": W.CONFIG_NAMES[n]}
+    if n == 4:
+        m = W.config4(pad=0, partition_size=args.partition_size)
+        dd, dp = Dev(m.decode), Dev(m.prefill)
+        s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, args.steps,
+                           args.warmup, flush)
+        pms = time_prefill(torch, pa, dp, m.prefill, args.steps, args.warmup, flush)
+        pre_ms = sum(pms) / len(pms)
+        res["decode"] = decode_summary(m.decode, s, k)
+        res["prefill_ms"] = round(pre_ms, 5)
+        res["prefill_TFLOPs"] = round(m.prefill.flops() / pre_ms / 1e9, 2)
+    else:
+        w = W.config3(pad=0) if n == 3 else W.config5(pad=0, partition_size=args.partition_size)
+        dd = Dev(w)
+        s, k = time_decode(torch, pa, dd, w, w.partition_size, args.steps, args.warmup, flush)
+        res.update(decode_summary(w, s, k))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +235,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5"],
+                    help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
+                         "plus the others under per_config)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -166,6 +252,8 @@ def main():
         sys.exit(2)
 
     import workloads as W
+    if args.workload != "C2":
+        return profile_one(args, W)
     wl = W.config2(pad=0, partition_size=args.partition_size)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)   # before any GPU use
 
@@ -178,9 +266,14 @@ def main():
     d = Dev(wl)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ms, kern_ms = time_decode(torch, pa, d, wl, args.partition_size, args.steps,
-                                   args.warmup, flush)
+    step_ms, _ = time_decode(torch, pa, d, wl, args.partition_size, args.steps,
+                             args.warmup, flush)
     wall = time.perf_counter() - t0
+    if args.partition_size > 0:   # the dominant kernel on its own
+        kern_ms = time_partition_kernel(torch, pa, d, wl, args.partition_size, args.steps,
+                                        args.warmup, flush)
+    else:
+        kern_ms = step_ms
     head = decode_summary(wl, step_ms, kern_ms)
     del d
 
@@ -237,15 +330,19 @@ def main():
                    "note": "per-step HIP events around the launches; a 1 GiB rewrite before "
                            "each step evicts the Infinity Cache and is not timed"},
         "roofline": {
-            "kernel": "decode_kernel<128, bf16, split>",
+            "kernel": "decode_kernel<128, bf16, split> (pa_decode_partitions)",
             "bound": "hbm",
             "achieved": head["partition_kernel_GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["partition_kernel_GBps"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(args.partition_size),
             "algorithmic_bytes_per_launch": head["kv_bytes"],
             "avg_launch_ms": head["partition_kernel_ms"],
+            "note": "achieved = live K+V bytes / mean HIP-event duration of the partition "
+                    "kernel launched alone; traffic = HBM bytes read+written per launch from "
+                    "the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), "
+                    "null if the kernel sources changed since",
         },
         "cpu_baseline": cpu,
         "per_config": per_config,
