@@ -13,8 +13,10 @@
 //     (K as the A operand exactly as it sits in the token-major tile, Q^T as
 //     the B operand, heads >= G padded with zeros);
 //   * online softmax in base 2: each lane owns one head (its column r) and
-//     four tokens; block max / sum are reduced over the four lane groups with
-//     row-swap permutes;
+//     four tokens; the block max is reduced over the four lane groups with
+//     row-swap permutes, the row sum only once at the end; the running max is
+//     refreshed (and the accumulator rescaled) only when it jumps by more than
+//     kRescaleLog2;
 //   * O^T[d x 16 heads] += V^T_blk . P^T on MFMA; the dim-major V tile makes
 //     V^T the A operand with each lane reading four consecutive tokens;
 //   * a workgroup of 4 waves shares one (sequence, kv-head, partition): wave
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     constexpr int NT = T::NT;
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;  // wave of the workgroup
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, known uniform
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
         float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
         bm = group_max4(bm);
         const float mn = fmaxf(m, bm);
-        if (__ballot(mn > m)) {  // some column's max moved: rescale
+        if (__ballot((mn - m) * C > kRescaleLog2)) {  // some column's max jumped: rescale
             const float alpha = fast_exp2((m - mn) * C);
             l *= alpha;
 #pragma unroll
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - m) * C);
-        l += group_sum4((p[0] + p[1]) + (p[2] + p[3]));
+        l += (p[0] + p[1]) + (p[2] + p[3]);  // this lane's tokens; reduced after the loop
         T::pv(R, p, acc);
     };
 
@@ -158,6 +160,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
             consume(b0, i);
         }
     }
+
+    l = group_sum4(l);
 
     // ---- combine the waves' softmax states through LDS (wave 0 holds the result)
     constexpr int kCombineFloats = (WAVES - 1) * (NT * 4 * 64 + 32);

@@ -26,6 +26,12 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax keeps a column's running max until a block raises it by
+// more than this many log2 units; weights then stay below 2^8, far inside
+// fp32 and bf16 range, and the normalisation uses the same weights, so the
+// result is unchanged up to rounding.  A larger jump rescales, which leaves
+// the new maximum's weight exactly exp2(0) = 1.
+constexpr float kRescaleLog2 = 8.0f;
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 

@@ -8,13 +8,18 @@
 // ctx + i (ctx = L - n), attending to keys 0 .. ctx + i.
 //
 // Layout of the work.  The chunk's (query, head-of-group) pairs are numbered
-// rho = i * G + g and cut into 16-wide column tiles; one wave owns NC tiles
-// of one (chunk, kv-head).  For each 16-token key block the wave computes
-// S^T = K_blk . Q^T for each of its tiles on MFMA, runs the online softmax
-// per column (base 2), and accumulates O^T += V^T_blk . P^T.  Every block is
-// loaded once per wave and used by all NC tiles; blocks wholly below the
-// diagonal skip the causal mask.  Blocks shared by several chunks (a common
-// prefix) are simply read through each chunk's table.
+// rho = i * G + g and cut into 16-wide MFMA column tiles.  A workgroup of 4
+// waves owns 4 * NC tiles of one (chunk, kv-head); each wave owns NC tiles.
+// Key blocks go two at a time through a double-buffered LDS stage: the
+// workgroup loads a step's K and V tiles once, every thread one or more
+// contiguous 16-byte pieces (plain loads, so blocks that several chunks share
+// -- a common prefix -- can be served by L2), while the previous step is
+// computed; one barrier per step.  K tiles keep their HBM layout in LDS and V
+// rows are padded by 8 bytes, so each wave reads its MFMA operands the way
+// decode reads them from HBM, without LDS bank conflicts.  Per block and
+// column tile: S^T = K . Q^T on MFMA, online softmax per column (base 2),
+// then O^T += V^T . P^T.  Blocks wholly below a wave's diagonal skip the
+// mask; row sums stay per lane until the end.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -22,13 +27,25 @@
 namespace pa {
 namespace {
 
+constexpr int kWaves = 4;
+constexpr int kStepBlocks = 2;  // key blocks per LDS stage (consumed as a pair)
+
 template <int D, int KIND, int NC>
-__global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
+    constexpr int TB = T::kTileBytes;                       // one K (or V) tile in HBM
+    constexpr int kVLds = D * T::kVRowLds;                   // one V tile in LDS (padded rows)
+    constexpr int kSlot = (TB + kVLds + 15) / 16 * 16;       // K then V of one block
+    constexpr int kPieces = kStepBlocks * 2 * TB / 16;       // 16-byte pieces per step
+    constexpr int kPerThread = kPieces / (64 * kWaves);
+    static_assert(kPieces % (64 * kWaves) == 0, "every thread loads whole pieces");
+    __shared__ __attribute__((aligned(16))) char stage[2][kStepBlocks][kSlot];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
@@ -38,14 +55,16 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
     const int L = a.seq_lens[ch];
     const int ctx = L - qlen;
     const int nrho = qlen * G;
-    const int rho0 = blockIdx.y * (16 * NC);
-    if (rho0 >= nrho || ctx < 0) return;  // ctx < 0 breaks the contract: read nothing
+    const int rho_wg = blockIdx.y * (16 * NC * kWaves);
+    if (rho_wg >= nrho || ctx < 0) return;  // uniform; ctx < 0 breaks the contract: read nothing
 
-    const int last_rho = min(nrho, rho0 + 16 * NC) - 1;
-    const int pos_max = ctx + last_rho / G;  // largest query position in this wave
-    const int pos_min = ctx + rho0 / G;      // smallest
-    const int nblk = pos_max / kBS + 1;      // key blocks anyone here sees
-    const int full_end = (pos_min + 1) / kBS; // blocks below need no causal mask
+    // key blocks the workgroup needs, and this wave's share of the rows
+    const int nblk = (ctx + (min(nrho, rho_wg + 16 * NC * kWaves) - 1) / G) / kBS + 1;
+    const int rho0 = rho_wg + w * 16 * NC;
+    const bool wave_rows = rho0 < nrho;
+    const int w_last = min(nrho, rho0 + 16 * NC) - 1;
+    const int w_nblk = wave_rows ? (ctx + w_last / G) / kBS + 1 : 0;   // blocks this wave sees
+    const int full_end = wave_rows ? (ctx + rho0 / G + 1) / kBS : 0;   // no mask below this
 
     int pos[NC];
     bool ok[NC];
@@ -56,26 +75,57 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
         const int rho = rho0 + 16 * ct + r;
         ok[ct] = rho < nrho;
         const int i = rho / G, g = rho - (rho / G) * G;
-        pos[ct] = ok[ct] ? ctx + i : pos_max;
+        pos[ct] = ok[ct] ? ctx + i : ctx + w_last / G;
         qrow_idx[ct] = (qbeg + i) * Hq + h * G + g;
         T::load_q(Q[ct], ok[ct] ? reinterpret_cast<const QT*>(a.q) + (size_t)qrow_idx[ct] * D : nullptr, c);
     }
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;
 
+    // block-table window (every wave holds the same 64 entries)
     const int32_t* trow = a.block_table + (size_t)ch * a.max_blocks_per_seq;
     int tbase = 0;
     int tcur = (lane < nblk) ? trow[lane] : 0;
-    int tnxt = (64 + lane < nblk) ? trow[64 + lane] : 0;
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
-    const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
-    auto issue = [&](typename T::Regs& R, int jb) {
-        const int idx = jb - tbase;
-        const int phys = idx < 64 ? __builtin_amdgcn_readlane(tcur, idx)
-                                  : __builtin_amdgcn_readlane(tnxt, idx - 64);
-        const size_t off = (size_t)phys * blk_stride;
-        T::load(R, kbase + off, vbase + off, r, c);
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * TB;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * TB;
+    const size_t blk_stride = (size_t)Hkv * TB;
+
+    // global -> registers for one step: piece p is byte 16 * (p % (TB/16)) of
+    // tile p / (TB/16) = (block of the step, K or V)
+    u32x4 held[kPerThread];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int p = tid + u * 64 * kWaves;
+            const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
+            const int jb = min(j0 + (tile >> 1), nblk - 1);  // a missing 2nd block re-reads the 1st
+            const int phys = __shfl(tcur, jb - tbase, 64);
+            const char* src = ((tile & 1) ? vbase : kbase) + (size_t)phys * blk_stride + off;
+            held[u] = ld16(src);
+        }
+    };
+    // registers -> LDS: K tiles verbatim, V rows re-strided to T::kVRowLds
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int p = tid + u * 64 * kWaves;
+            const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
+            char* slot = stage[buf][tile >> 1];
+            if (!(tile & 1)) {
+                *reinterpret_cast<u32x4*>(slot + off) = held[u];
+            } else {
+                char* dst = slot + TB + (off / T::kVRow) * T::kVRowLds + off % T::kVRow;
+                if constexpr (T::kVRowLds % 16 == 0) {
+                    *reinterpret_cast<u32x4*>(dst) = held[u];
+                } else if constexpr (T::kVRowLds % 8 == 0) {
+                    reinterpret_cast<u32x2*>(dst)[0] = u32x2{held[u].x, held[u].y};
+                    reinterpret_cast<u32x2*>(dst)[1] = u32x2{held[u].z, held[u].w};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) reinterpret_cast<unsigned*>(dst)[e] = held[u][e];
+                }
+            }
+        }
     };
 
     float m[NC], l[NC];
@@ -88,68 +138,75 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
         for (int n = 0; n < NT; ++n) acc[ct][n] = zero4();
     }
 
-    // one key block against every column tile of the wave
-    auto consume = [&](typename T::Regs& R, int jj) {
-        const int valid = L - jj * kBS;
-        if (valid < kBS) T::mask_v(R, c, valid);  // cache slots past L
-        const bool diag = jj >= full_end;
+    // The two blocks of a step (jA, jA+1) against every column tile of this
+    // wave: 8 scores per lane, one online-softmax round over 32 keys, one
+    // K=32 MFMA per output tile.  A block the wave does not need (past its
+    // diagonal, or past the sequence) has all its scores masked to -inf and
+    // its V zeroed, so it adds exactly nothing.
+    auto consume2 = [&](int buf, int jA) {
+        typename T::Regs RA, RB;
+        T::load_lds(RA, stage[buf][0], stage[buf][0] + TB, r, c);
+        T::load_lds(RB, stage[buf][1], stage[buf][1] + TB, r, c);
+        const int jB = jA + 1;
+        const bool needB = jB < w_nblk;
+        const int validA = L - jA * kBS;
+        const int validB = needB ? L - jB * kBS : 0;
+        if (validA < kBS) T::mask_v(RA, c, validA);  // cache slots past L
+        if (validB < kBS) T::mask_v(RB, c, validB);
+        const bool diag = jB >= full_end || !needB;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            const f32x4 sc = T::qk(R, Q[ct]);   // raw scores, as in decode
-            float t[4] = {sc[0], sc[1], sc[2], sc[3]};
+            const f32x4 sa = T::qk(RA, Q[ct]);   // raw scores, as in decode
+            const f32x4 sb = T::qk(RB, Q[ct]);
+            float t[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
             if (diag) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (jj * kBS + 4 * c + e > pos[ct]) t[e] = -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                    if (jA * kBS + 4 * c + e > pos[ct]) t[e] = -INFINITY;
+                    if (!needB || jB * kBS + 4 * c + e > pos[ct]) t[4 + e] = -INFINITY;
+                }
             }
-            float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+            float bm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                             fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
             bm = group_max4(bm);
             const float mn = fmaxf(m[ct], bm);
-            if (__ballot(mn > m[ct])) {
+            if (__ballot((mn - m[ct]) * C > kRescaleLog2)) {
                 const float alpha = fast_exp2((m[ct] - mn) * C);
                 l[ct] *= alpha;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
                 m[ct] = mn;
             }
-            float p[4];
+            float p[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - m[ct]) * C);
-            l[ct] += group_sum4((p[0] + p[1]) + (p[2] + p[3]));
-            T::pv(R, p, acc[ct]);
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2((t[e] - m[ct]) * C);
+            l[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            T::pv2(RA, RB, p, acc[ct]);
         }
     };
 
-    // two-stage pipeline with a peeled tail, as in decode
-    typename T::Regs b0, b1;
-    issue(b0, 0);
-    int j = 0;
-    for (; j + 2 < nblk; j += 2) {
-        if (j - tbase >= 64) {
-            tbase += 64;
-            tcur = tnxt;
-            tnxt = (tbase + 64 + lane < nblk) ? trow[tbase + 64 + lane] : 0;
+    const int nsteps = (nblk + kStepBlocks - 1) / kStepBlocks;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int j0 = s * kStepBlocks;
+        if (s + 1 < nsteps) {
+            if (j0 + 2 * kStepBlocks - 1 - tbase >= 64) {  // next step leaves the table window
+                tbase += 64 - kStepBlocks;                  // keep the 2 steps in one window
+                tcur = (tbase + lane < nblk) ? trow[tbase + lane] : 0;
+            }
+            fetch(j0 + kStepBlocks);  // in flight during this step's compute
         }
-        issue(b1, j + 1);
-        consume(b0, j);
-        issue(b0, j + 2);
-        consume(b1, j + 1);
-    }
-    if (j - tbase >= 64) {
-        tbase += 64;
-        tcur = tnxt;
-    }
-    if (j + 1 < nblk) {
-        issue(b1, j + 1);
-        consume(b0, j);
-        consume(b1, j + 1);
-    } else {
-        consume(b0, j);
+        if (j0 < w_nblk) consume2(s & 1, j0);
+        if (s + 1 < nsteps) stash((s + 1) & 1);
+        __syncthreads();
     }
 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
+        l[ct] = group_sum4(l[ct]);
         if (!ok[ct]) continue;
         const float inv = vscale / l[ct];
         QT* o = reinterpret_cast<QT*>(a.out) + (size_t)qrow_idx[ct] * D;
@@ -167,8 +224,9 @@ template <int D, int KIND>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const long rows = (long)a.max_q_len * G;
-    dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + 16 * kNC - 1) / (16 * kNC)));
-    hipLaunchKernelGGL((prefill_kernel<D, KIND, kNC>), grid, dim3(64), 0, s, a);
+    const long per_wg = 16L * kNC * kWaves;
+    dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + per_wg - 1) / per_wg));
+    hipLaunchKernelGGL((prefill_kernel<D, KIND, kNC>), grid, dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 

@@ -47,6 +47,15 @@ template <int D> struct Tile<KV_BF16, D> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (kBS * 2) + c * 8);
     }
+    // the same lane layout read from a tile staged in LDS (plain loads)
+    // V rows in LDS are kVRowLds bytes apart (padded: conflict-free reads)
+    static constexpr int kVRow = kBS * 2, kVRowLds = kVRow + 8;
+    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld8(vt + (16 * n + r) * kVRowLds + c * 8);
+    }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();
 #pragma unroll
@@ -66,6 +75,15 @@ template <int D> struct Tile<KV_BF16, D> {
         pb.y = pack_bf16x2(p[2], p[3]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(R.v[n], pb, acc[n]);
+    }
+    // two blocks in one K=32 product: k-slots (c, 0..3) are block A's tokens
+    // 4c..4c+3 and (c, 4..7) block B's, matching p[0..3] / p[4..7]
+    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
+        const u32x4 pb{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            acc[n] = mfma_16x16x32_bf16(u32x4{A.v[n].x, A.v[n].y, B.v[n].x, B.v[n].y}, pb, acc[n]);
     }
 };
 
@@ -90,6 +108,13 @@ template <int D> struct Tile<KV_FP8, D> {
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * kBS + c * 4);
+    }
+    static constexpr int kVRow = kBS, kVRowLds = kVRow + 4;
+    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld4(vt + (16 * n + r) * kVRowLds + c * 4);
     }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();
@@ -117,6 +142,15 @@ template <int D> struct Tile<KV_FP8, D> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(fp8x4_to_bf16x4(R.v[n]), pb, acc[n]);
     }
+    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
+        const u32x4 pb{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const u32x2 a = fp8x4_to_bf16x4(A.v[n]), b = fp8x4_to_bf16x4(B.v[n]);
+            acc[n] = mfma_16x16x32_bf16(u32x4{a.x, a.y, b.x, b.y}, pb, acc[n]);
+        }
+    }
 };
 
 template <int D> struct Tile<KV_F32, D> {
@@ -137,6 +171,13 @@ template <int D> struct Tile<KV_F32, D> {
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (kBS * 4) + c * 16);
+    }
+    static constexpr int kVRow = kBS * 4, kVRowLds = kVRow + 16;
+    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) R.v[n] = ld16(vt + (16 * n + r) * kVRowLds + c * 16);
     }
     __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
         f32x4 s = zero4();
@@ -161,6 +202,10 @@ template <int D> struct Tile<KV_F32, D> {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 acc[n] = mfma_16x16x4_f32(__uint_as_float(R.v[n][e]), p[e], acc[n]);
+    }
+    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
+        pv(A, p, acc);
+        pv(B, p + 4, acc);
     }
 };
 
