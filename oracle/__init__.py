@@ -9,11 +9,12 @@ the seeded inputs from ``workloads``.
 Everything is float64 numpy, written as the plain definition (see
 ``oracle.attention``).  Every function is pinned by CPU tests against
 closed forms, a dense library routine, invariants and brute force
-(``tests/test_oracle_pins.py``).
+(``tests/test_oracle_pins.py``; the fp8 encoder and the cache writer in
+``tests/test_oracle_write_pins.py``).
 """
 from .attention import (decode, decode_partials, merge, prefill_chunk, gather_kv, attend,
-                        widen, round_to, items_for)
+                        widen, round_to, items_for, write_kv)
 from . import fp8_e4m3
 
 __all__ = ["decode", "decode_partials", "merge", "prefill_chunk", "gather_kv", "attend",
-           "widen", "round_to", "items_for", "fp8_e4m3"]
+           "widen", "round_to", "items_for", "write_kv", "fp8_e4m3"]

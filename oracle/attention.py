@@ -249,3 +249,39 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
 def items_for(seq_ids: Sequence[int], Hkv: int):
     """All (sequence, kv-head) pairs of the given sequences."""
     return [(int(b), h) for b in seq_ids for h in range(Hkv)]
+
+
+# ---------------------------------------------------------------------------
+# writing new tokens into the paged cache
+# ---------------------------------------------------------------------------
+def write_kv(k_cache, v_cache, key, value, slot_mapping, in_dtype: str, kv_dtype: str,
+             k_scale=None, v_scale=None):
+    """Store the K/V rows of new tokens into their cache slots (in place).
+
+    Token t goes to slot s = slot_mapping[t] = physical block * bs + offset;
+    s < 0 marks a padding token that is skipped.  bf16 / fp32 caches receive
+    the values as they are (same storage type as the input).  An fp8 cache
+    receives e4m3fn(x / scale[kv_head]): fp32 true division, then round to
+    nearest even with saturation at 448 (the amax / 448 scale rule of
+    vllm-metis 0.1.0, "Status", applied on write).
+    """
+    bs = v_cache.shape[3]
+    T, Hkv, d = key.shape
+    kx = k_cache.shape[4]
+    for t in range(T):
+        s = int(slot_mapping[t])
+        if s < 0:
+            continue
+        phys, off = s // bs, s % bs
+        for h in range(Hkv):
+            kr, vr = key[t, h], value[t, h]
+            if kv_dtype == "fp8":
+                kq = fp8_e4m3.encode(widen(kr, in_dtype).astype(np.float32) / np.float32(k_scale[h]))
+                vq = fp8_e4m3.encode(widen(vr, in_dtype).astype(np.float32) / np.float32(v_scale[h]))
+            elif kv_dtype == in_dtype:
+                kq, vq = kr, vr
+            else:
+                raise ValueError("a bf16 / fp32 cache takes inputs of its own type")
+            k_cache[phys, h, :, off, :] = np.asarray(kq).reshape(d // kx, kx)
+            v_cache[phys, h, :, off] = vq
+    return k_cache, v_cache

@@ -45,3 +45,35 @@ _TABLE = table()
 def decode(codes: np.ndarray) -> np.ndarray:
     """Decode an array of uint8 codes to float64 (exact)."""
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# ---------------------------------------------------------------------------
+# encoding: round to nearest, ties to even, saturating at +-448
+# ---------------------------------------------------------------------------
+_FINITE_CODES = np.array([c for c in range(0x00, 0x7F)], dtype=np.int64)   # 0 .. 0x7E: +0 .. 448
+_FINITE_VALUES = _TABLE[_FINITE_CODES]                                     # increasing
+
+
+def encode(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> e4m3fn codes, nearest representable value, ties to the
+    code with an even mantissa, magnitudes above 448 saturated to 448 (the
+    cache-write reading: saturate, never produce NaN from a finite input).
+
+    Works on magnitudes: the positive codes 0x00..0x7E are increasing in value,
+    so the two neighbours of |x| are adjacent codes and the tie rule picks the
+    even one (mantissa lsb 0).  NaN inputs give the NaN code 0x7F (sign kept).
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)   # exact widening
+    sign = np.signbit(x)
+    a = np.abs(x)
+    a = np.minimum(a, E4M3_MAX)
+    hi = np.searchsorted(_FINITE_VALUES, a, side="left")       # first value >= a
+    hi = np.minimum(hi, len(_FINITE_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    v_hi, v_lo = _FINITE_VALUES[hi], _FINITE_VALUES[lo]
+    d_hi, d_lo = v_hi - a, a - v_lo
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_FINITE_CODES[hi] % 2 == 0))
+    pick_hi |= (v_hi == a)
+    code = np.where(pick_hi, _FINITE_CODES[hi], _FINITE_CODES[lo])
+    code = np.where(np.isnan(a), 0x7F, code)
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
