@@ -218,7 +218,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     }
 }
 
-constexpr int kNC = 2;
+#ifndef PA_PREFILL_NC
+#define PA_PREFILL_NC 2
+#endif
+constexpr int kNC = PA_PREFILL_NC;
 
 template <int D, int KIND>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
