@@ -47,7 +47,9 @@
  * slots past seq_len are never read (they may hold anything, NaN included).
  *
  * Errors.  A non-zero pa_status is returned before anything is enqueued when
- * the arguments are invalid.  PA_ERR_HIP reports a failed launch (including a
+ * the arguments are invalid.  A call with nothing to do (num_seqs == 0,
+ * num_chunks == 0 or max_q_len == 0, num_tokens == 0) validates its sizes,
+ * launches nothing and accepts NULL for its arrays.  PA_ERR_HIP reports a failed launch (including a
  * library built without a gfx950 code object).  There is no fallback path.
  * Block-table contents are not checked: an entry outside [0, num_blocks) or
  * a seq_len above max_blocks_per_seq * block_size is undefined behaviour.
@@ -169,6 +171,40 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                      int num_blocks, float scale, const float* k_scale,
                      const float* v_scale, void* stream);
+
+/*
+ * Cache write: store the K/V rows of num_tokens new tokens into their cache
+ * slots, the step that precedes attention in every decode step and prefill
+ * chunk (the cache is addressed by (block, offset) through block tables:
+ * vllm-metal architecture article, section 四; FP8 with one scale of
+ * amax / 448: vllm-metis 0.1.0, "Status").
+ *
+ * key, value       rows of token t at key + t * key_stride elements, laid out
+ *                  [num_kv_heads, head_dim] (contiguous inside a row); a stride
+ *                  above num_kv_heads * head_dim lets K and V be views into a
+ *                  fused projection output.  in_dtype PA_F32 or PA_BF16;
+ *                  16-byte aligned, and stride * element size a multiple of 16.
+ * slot_mapping     int32 [num_tokens]: token t goes to physical block
+ *                  slot / block_size, offset slot % block_size.  A negative
+ *                  slot marks a padding token and is skipped; so is a slot at
+ *                  or beyond num_blocks * block_size (no write lands outside
+ *                  the caches).  Two tokens mapped to one slot race.
+ * k_cache, v_cache the layouts above, kv_dtype equal to in_dtype (an exact
+ *                  copy) or PA_FP8_E4M3.  An fp8 cache receives
+ *                  e4m3fn(x / scale[kv_head]): the fp32 value of the input
+ *                  divided by the fp32 scale (correctly rounded), clamped to
+ *                  [-448, 448], rounded to the nearest code, ties to the even
+ *                  code.  Inputs must be finite (a NaN gives an unspecified
+ *                  code); k_scale and v_scale must be finite and > 0.
+ * Slots not named by slot_mapping are left untouched.  With num_tokens == 0
+ * nothing is launched, and key, value and slot_mapping may be NULL.
+ */
+int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype,
+                const void* key, const void* value, int in_dtype,
+                int key_stride, int value_stride,
+                const int32_t* slot_mapping, int num_tokens,
+                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                const float* k_scale, const float* v_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,8 @@ SIGNATURES = {
     "pa_merge_partitions": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "pa_prefill_chunk": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
                               _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
+    "pa_write_kv": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp,
+                         _vp]),
 }
 
 
@@ -43,7 +45,7 @@ class PAError(RuntimeError):
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m paged_kv_cache_22_amd.build`")
+        raise ImportError(f"{path} is not built; run `python paged_kv_cache_22_amd/build.py`")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -211,3 +213,44 @@ def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, *, max_
                               _dev(v_scale, "v_scale"), _stream(q))
     _check("pa_prefill_chunk", st)
     return (out, out_lse) if want_lse else out
+
+
+def _rows(t, name: str):
+    """Pointer and token stride (elements) of a [T, Hkv, d] tensor whose last
+    two dims are contiguous (a view into a wider projection output is fine)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libpa has no CPU path)")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [T, Hkv, d]")
+    T, H, D = t.shape
+    row = H * D
+    if t.numel() == 0:
+        return t.data_ptr(), row
+    # strides of size-1 dims carry no meaning
+    if (D > 1 and t.stride(2) != 1) or (H > 1 and t.stride(1) != D):
+        raise ValueError(f"{name} must be [T, Hkv, d] with contiguous (Hkv, d) rows")
+    return t.data_ptr(), t.stride(0) if T > 1 else row
+
+
+def write_kv(key, value, k_cache, v_cache, slot_mapping, *, k_scale=None, v_scale=None):
+    """Store new tokens' K/V rows into their cache slots (pa_write_kv), in place.
+    key/value [T, Hkv, d] (f32 or bf16); fp8 caches quantise with the per-kv-head
+    scales."""
+    T, Hkv, d = key.shape
+    if tuple(value.shape) != (T, Hkv, d):
+        raise ValueError("value must have key's shape")
+    NB, Hkv_c, nchunk, bs, x = k_cache.shape
+    if Hkv_c != Hkv or nchunk * x != d or x * k_cache.element_size() != 16:
+        raise ValueError("k_cache must be [NB, Hkv, d/X, bs, X] matching key")
+    if tuple(v_cache.shape) != (NB, Hkv, d, bs):
+        raise ValueError("v_cache must be [NB, Hkv, d, bs]")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must be [T]")
+    kp, ks_ = _rows(key, "key")
+    vp, vs_ = _rows(value, "value")
+    st = lib.pa_write_kv(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                         _dtype_code(k_cache, True), kp, vp, _dtype_code(key, False),
+                         int(ks_), int(vs_), _dev(slot_mapping, "slot_mapping"), T, Hkv, d, bs,
+                         NB, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(key))
+    _check("pa_write_kv", st)
+    return k_cache, v_cache

@@ -1,6 +1,6 @@
 """Build libpa.so (HIP kernels for gfx950 + the C-ABI front end), in-tree.
 
-    python -m paged_kv_cache_22_amd.build
+    python paged_kv_cache_22_amd/build.py
 
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 and ``csrc/api.cpp`` as
 host C++, then links ``paged_kv_cache_22_amd/libpa.so``.  Always rebuilds.

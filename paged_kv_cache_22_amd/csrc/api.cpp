@@ -28,15 +28,16 @@ int dtype_ok(int q_dtype, int kv_dtype) {
     return ok ? PA_OK : PA_ERR_DTYPE;
 }
 
-// checks shared by decode and prefill
+// checks shared by decode and prefill; `empty` = the call launches nothing,
+// so its arrays may be empty (NULL)
 int common_checks(const void* q, const void* k_cache, const void* v_cache, int q_dtype, int kv_dtype,
                   const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                  float scale, const float* k_scale, const float* v_scale) {
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens) return PA_ERR_NULL;
+                  float scale, const float* k_scale, const float* v_scale, bool empty) {
+    if (!empty && (!q || !k_cache || !v_cache || !block_table || !seq_lens)) return PA_ERR_NULL;
     int st = dtype_ok(q_dtype, kv_dtype);
     if (st != PA_OK) return st;
-    if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!empty && kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
     if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         num_blocks < 0 || max_blocks_per_seq <= 0)
         return PA_ERR_SHAPE;
@@ -58,7 +59,7 @@ int decode_checks(const void* q, int q_dtype, const void* k_cache, const void* v
                   int partition_size, int max_seq_len) {
     int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
                            seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                           scale, k_scale, v_scale);
+                           scale, k_scale, v_scale, num_seqs == 0);
     if (st != PA_OK) return st;
     if (num_seqs < 0 || max_seq_len < 0) return PA_ERR_SHAPE;
     if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
@@ -141,7 +142,7 @@ int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partiti
                            num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
     if (st != PA_OK) return st;
     if (partition_size == 0) return PA_ERR_UNSUPPORTED;
-    if (!partial_out || !partial_lse) return PA_ERR_NULL;
+    if (num_seqs > 0 && (!partial_out || !partial_lse)) return PA_ERR_NULL;
     if (!aligned16(partial_out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u)) return PA_ERR_ALIGN;
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
     if (max_partitions < parts) return PA_ERR_SHAPE;
@@ -160,7 +161,7 @@ int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partiti
 int pa_merge_partitions(void* out, int out_dtype, float* out_lse, const float* partial_out,
                         const float* partial_lse, const int32_t* seq_lens, int partition_size,
                         int max_partitions, int num_seqs, int num_q_heads, int head_dim, void* stream) {
-    if (!out || !partial_out || !partial_lse || !seq_lens) return PA_ERR_NULL;
+    if (num_seqs != 0 && (!out || !partial_out || !partial_lse || !seq_lens)) return PA_ERR_NULL;
     if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
     if (num_seqs < 0 || num_q_heads <= 0 || max_partitions < 0 || partition_size <= 0)
         return PA_ERR_SHAPE;
@@ -195,7 +196,7 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
                            seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
     if (st != PA_OK) return st;
-    if (!out) return PA_ERR_NULL;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
     if (!aligned16(out)) return PA_ERR_ALIGN;
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
                                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
@@ -209,7 +210,7 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
     }
     const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
                                                  partition_size);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (num_seqs > 0 && need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
     if (num_seqs == 0) return PA_OK;
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
@@ -254,11 +255,12 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, cons
                      const int32_t* seq_lens, int num_chunks, int num_q_heads, int num_kv_heads,
                      int head_dim, int block_size, int num_blocks, float scale, const float* k_scale,
                      const float* v_scale, void* stream) {
+    const bool empty = num_chunks == 0 || max_q_len == 0;
     int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
                            seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                           scale, k_scale, v_scale);
+                           scale, k_scale, v_scale, empty);
     if (st != PA_OK) return st;
-    if (!out || !cu_q_lens) return PA_ERR_NULL;
+    if (!empty && (!out || !cu_q_lens)) return PA_ERR_NULL;
     if (!aligned16(out) || (reinterpret_cast<uintptr_t>(cu_q_lens) & 3u) ||
         (reinterpret_cast<uintptr_t>(out_lse) & 3u))
         return PA_ERR_ALIGN;
@@ -289,6 +291,51 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, cons
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale = scale;
     return hip_status(pa::launch_prefill(a, stream));
+}
+
+int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype, const void* key, const void* value,
+                int in_dtype, int key_stride, int value_stride, const int32_t* slot_mapping,
+                int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                const float* k_scale, const float* v_scale, void* stream) {
+    // with no tokens the per-token arrays may be empty (NULL)
+    const bool none = num_tokens == 0;
+    if (!k_cache || !v_cache || (!none && (!key || !value || !slot_mapping))) return PA_ERR_NULL;
+    if (in_dtype != PA_F32 && in_dtype != PA_BF16) return PA_ERR_DTYPE;
+    if (kv_dtype != PA_FP8_E4M3 && kv_dtype != in_dtype) return PA_ERR_DTYPE;
+    if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    const long long row = (long long)num_kv_heads * head_dim;
+    if (key_stride < row || value_stride < row) return PA_ERR_SHAPE;
+    if ((long long)num_blocks * block_size > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const int in_bytes = in_dtype == PA_BF16 ? 2 : 4;
+    if (((long long)key_stride * in_bytes) % 16 || ((long long)value_stride * in_bytes) % 16)
+        return PA_ERR_ALIGN;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(key) || !aligned16(value) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
+        return PA_ERR_ALIGN;
+    const int chunk = kv_dtype == PA_FP8_E4M3 ? 16 : kv_dtype == PA_BF16 ? 8 : 4;
+    if (((long long)num_kv_heads * (head_dim / chunk) + 3) / 4 > kMaxGridY) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    pa::WriteArgs a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.key = key;
+    a.value = value;
+    a.slot_mapping = slot_mapping;
+    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    a.key_stride = key_stride;
+    a.value_stride = value_stride;
+    a.in_dtype = in_dtype;
+    a.kv_dtype = kv_dtype;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.num_blocks = num_blocks;
+    return hip_status(pa::launch_write_kv(a, stream));
 }
 
 }  // extern "C"

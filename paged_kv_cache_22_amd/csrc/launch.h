@@ -61,9 +61,23 @@ struct PrefillArgs {
     float scale;
 };
 
+struct WriteArgs {
+    void* k_cache;
+    void* v_cache;
+    const void* key;          // [num_tokens, token stride] rows, (kv-head, dim) inside
+    const void* value;
+    const int32_t* slot_mapping;
+    const float* k_scale;     // fp8 cache only
+    const float* v_scale;
+    long long key_stride, value_stride;   // elements between consecutive tokens
+    int in_dtype, kv_dtype;   // pa_dtype
+    int num_tokens, num_kv_heads, head_dim, num_blocks;
+};
+
 // Each returns 0 on success or the hipError_t of a failed launch.
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
+int launch_write_kv(const WriteArgs& a, void* stream);
 
 }  // namespace pa

@@ -124,3 +124,82 @@ def test_binding_refuses_cpu_tensors():
     sl = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU tensor"):
         pa.decode(q, k, v, bt, sl, max_seq_len=1, out=torch.zeros_like(q))
+
+
+def write_call(**over):
+    a = dict(k=P, v=P, kv=1, key=P, value=P, ind=1, kst=1024, vst=1024, slots=P, T=64, hkv=8,
+             d=128, bs=16, nb=9000, ks=None, vs=None, stream=None)
+    a.update(over)
+    return pa.lib.pa_write_kv(a["k"], a["v"], a["kv"], a["key"], a["value"], a["ind"], a["kst"],
+                              a["vst"], a["slots"], a["T"], a["hkv"], a["d"], a["bs"], a["nb"],
+                              a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(slots=None), NULL),
+    (dict(key=None), NULL),
+    (dict(kv=2), NULL),                       # fp8 cache without scales
+    (dict(kv=0), DTYPE),                      # bf16 input into an fp32 cache
+    (dict(ind=2), DTYPE),                     # fp8 is not an input type
+    (dict(ind=7, kv=7), DTYPE),
+    (dict(d=96), UNSUP),
+    (dict(bs=32), UNSUP),
+    (dict(T=-1), SHAPE),
+    (dict(kst=1023), SHAPE),                  # stride shorter than a token's row
+    (dict(kst=1028), ALIGN),                  # row start not 16-byte aligned
+    (dict(value=P + 8), ALIGN),
+    (dict(slots=P + 2), ALIGN),
+    (dict(nb=1 << 28), SHAPE),                # slot numbers would overflow int32
+])
+def test_write_kv_rejects(over, status):
+    assert write_call(**over) == status
+
+
+def test_write_kv_accepts_empty():
+    assert write_call(T=0) == OK              # nothing to launch
+    assert write_call(T=0, key=None, value=None, slots=None) == OK
+    assert write_call(T=1, key=None) == NULL
+    assert write_call(T=0, kv=2, ks=P, vs=P, ind=0, kst=2048, vst=4096) == OK
+
+
+def test_build_script_loads_without_the_package():
+    """The build step must work in a tree where libpa.so does not exist yet,
+    so loading it must not import the package (whose import loads the library)."""
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g; m = g._build_module(); "
+            "assert callable(m.build); assert 'paged_kv_cache_22_amd' not in sys.modules")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_write_kv_binding_checks():
+    key = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 2, 8, 16, 8, dtype=torch.bfloat16)
+    vc = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16)
+    slots = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pa.write_kv(key, key, kc, vc, slots)
+    with pytest.raises(ValueError, match="shape"):
+        pa.write_kv(key, key[:2], kc, vc, slots)
+    with pytest.raises(ValueError, match="slot_mapping"):
+        pa.write_kv(key, key, kc, vc, slots[:2])
+
+
+def test_empty_calls_accept_null_arrays():
+    """Nothing to launch: sizes are still validated, arrays may be NULL."""
+    assert decode_call(num_seqs=0, out=None, q=None, k=None, v=None, bt=None, sl=None,
+                       ws=None, ws_bytes=0) == OK
+    assert decode_call(num_seqs=0, out=None, q=None, part=0) == OK
+    assert decode_call(num_seqs=0, q=None, d=96) == UNSUP        # sizes still checked
+    assert decode_call(num_seqs=1, q=None) == NULL
+    f = pa.lib.pa_decode_partitions
+    assert f(None, None, 8, None, 1, None, None, 1, None, 256, None, 0, 32, 8, 128, 16, 0,
+             0.08, None, None, 512, 4096, None) == OK
+    m = pa.lib.pa_merge_partitions
+    assert m(None, 1, None, None, None, None, 512, 8, 0, 32, 128, None) == OK
+    p = pa.lib.pa_prefill_chunk
+    assert p(None, None, None, 1, None, 0, 0, None, None, 1, None, 160, None, 0, 32, 8, 128, 16,
+             0, 0.08, None, None, None) == OK
+    assert p(None, None, None, 1, P, 0, 0, P, P, 1, P, 160, P, 4, 32, 8, 128, 16,
+             9000, 0.08, None, None, None) == OK                  # chunks all empty

@@ -122,6 +122,23 @@ def test_zero_length_sequence_gives_zeros():
         compare(got, ref, "bf16", f"zero-length P={P}")
 
 
+def test_empty_batch():
+    """No sequences: every entry point returns at once with empty tensors."""
+    import paged_kv_cache_22_amd as pa
+    q = torch.empty((0, 32, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((2, 8, 16, 16, 8), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((2, 8, 128, 16), dtype=torch.bfloat16, device="cuda")
+    bt = torch.empty((0, 4), dtype=torch.int32, device="cuda")
+    sl = torch.empty((0,), dtype=torch.int32, device="cuda")
+    for P in (0, 512):
+        out = pa.decode(q, k, v, bt, sl, max_seq_len=64, partition_size=P)
+        assert out.shape == (0, 32, 128)
+    po, pl = pa.decode_partitions(q, k, v, bt, sl, max_seq_len=64, partition_size=32)
+    out = pa.merge_partitions(po, pl, sl, partition_size=32)
+    torch.cuda.synchronize()
+    assert po.shape[0] == 0 and out.shape == (0, 32, 128)
+
+
 def test_single_token_is_v0_exactly():
     for kv in ("f32", "bf16", "fp8"):
         qd = "f32" if kv == "f32" else "bf16"

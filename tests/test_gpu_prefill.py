@@ -35,6 +35,30 @@ def test_ragged_chunks(kv, d_head):
     assert np.abs(f64(lse) - ref_lse).max() < 1e-3
 
 
+def test_empty_chunks():
+    """Chunks with no new tokens among others, chunks that are all empty, and
+    no chunks at all."""
+    import paged_kv_cache_22_amd as pa
+    wl = W.prefill_workload(seed=230, q_lens=[0, 20, 0, 7], ctx_lens=[10, 0, 5, 30],
+                            num_q_heads=8, num_kv_heads=2, head_dim=128, q_dtype="bf16",
+                            kv_dtype="bf16")
+    ref, _ = oracle_prefill(wl)
+    compare(f64(run_prefill(Dev(wl))), ref, "bf16", "prefill with empty chunks")
+    wl = W.prefill_workload(seed=231, q_lens=[0, 0], ctx_lens=[3, 40], num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    d = Dev(wl)
+    assert d.q.shape[0] == 0
+    out = run_prefill(d)
+    assert out.shape == (0, 8, 128)
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    none = torch.empty((0,), dtype=torch.int32, device="cuda")
+    out = pa.prefill_chunk(q, torch.zeros(1, dtype=torch.int32, device="cuda"), d.k, d.v,
+                           torch.empty((0, 4), dtype=torch.int32, device="cuda"), none,
+                           max_q_len=0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 128)
+
+
 @pytest.mark.parametrize("G", [1, 3, 4, 16])
 def test_group_sizes(G):
     wl = W.prefill_workload(seed=210 + G, q_lens=[37, 100], ctx_lens=[50, 0], num_q_heads=2 * G,

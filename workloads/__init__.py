@@ -50,6 +50,7 @@ __all__ = [
     "DecodeWorkload", "PrefillWorkload", "MixedWorkload",
     "config1", "config2", "config3", "config4", "config5", "build_config",
     "decode_workload", "prefill_workload", "to_bf16_bits", "to_fp8_codes",
+    "WriteWorkload", "write_workload", "write_chunks", "write_decode_step",
     "kv_bytes_per_token", "CONFIG_NAMES",
 ]
 
@@ -400,3 +401,120 @@ def config5(pad: int = -1, partition_size: int = 512) -> DecodeWorkload:
 
 def build_config(n: int, **kw):
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)
+
+
+# ---------------------------------------------------------------------------
+# cache writes: new tokens' K/V rows and the slots they go to
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class WriteWorkload:
+    """K/V rows of new tokens, their slot mapping and the cache they are
+    written into (its initial contents are random bytes, so that untouched
+    slots can be told apart)."""
+    name: str
+    key: np.ndarray               # [T, Hkv, d] in in_dtype storage
+    value: np.ndarray
+    slot_mapping: np.ndarray      # int32 [T]; -1 = padding token
+    k_cache: np.ndarray           # [NB, Hkv, d/X, bs, X] in kv_dtype storage
+    v_cache: np.ndarray           # [NB, Hkv, d, bs]
+    in_dtype: str
+    kv_dtype: str
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+
+    @property
+    def num_tokens(self) -> int: return int(self.key.shape[0])
+    @property
+    def num_kv_heads(self) -> int: return int(self.key.shape[1])
+    @property
+    def head_dim(self) -> int: return int(self.key.shape[2])
+    @property
+    def num_blocks(self) -> int: return int(self.k_cache.shape[0])
+    @property
+    def block_size(self) -> int: return int(self.v_cache.shape[3])
+
+    def bytes_moved(self) -> int:
+        """Algorithmic HBM bytes of one write: every token's K and V rows and
+        its slot number are read; every token with a slot inside the pool has
+        its K and V rows written."""
+        ein = 2 if self.in_dtype == "bf16" else 4
+        ekv = {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
+        row = self.num_kv_heads * self.head_dim
+        live = int(((self.slot_mapping >= 0) &
+                    (self.slot_mapping < self.num_blocks * self.block_size)).sum())
+        return self.num_tokens * (2 * row * ein + 4) + live * 2 * row * ekv
+
+
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+
+
+def write_workload(*, seed: int, slot_mapping, num_kv_heads: int, head_dim: int,
+                   in_dtype: str, kv_dtype: str, num_blocks: int, block_size: int = BLOCK_SIZE,
+                   fill_cache: bool = True, name: str = "write") -> WriteWorkload:
+    """Rows N(0,1) (cast to bf16 for bf16 input); an fp8 cache gets the
+    per-kv-head amax/448 scale of the rows drawn here.  ``fill_cache`` draws
+    random bytes for the initial cache, else zeros."""
+    rng = np.random.default_rng([seed, 7])
+    slots = np.asarray(slot_mapping, dtype=np.int32)
+    T = len(slots)
+    shape = (T, num_kv_heads, head_dim)
+    k32 = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    v32 = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    if in_dtype == "bf16":
+        key, value = to_bf16_bits(k32), to_bf16_bits(v32)
+        kf = key.astype(np.uint32) << 16
+        vf = value.astype(np.uint32) << 16
+        kf, vf = kf.view(np.float32), vf.view(np.float32)
+    else:
+        key, value, kf, vf = k32, v32, k32, v32
+    ks = vs = None
+    if kv_dtype == "fp8":
+        amax = lambda x: np.abs(x).max(axis=(0, 2)) if T else np.ones(num_kv_heads, np.float32)
+        ks = (amax(kf).astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
+        vs = (amax(vf).astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
+    x = chunk_dims(kv_dtype)
+    st = _STORAGE[kv_dtype]
+    kshape = (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+    vshape = (num_blocks, num_kv_heads, head_dim, block_size)
+    nbytes = int(np.prod(kshape)) * np.dtype(st).itemsize
+    if fill_cache:
+        crng = np.random.default_rng([seed, 8])
+        kc = crng.integers(0, 256, nbytes, dtype=np.uint8).view(st).reshape(kshape)
+        vc = crng.integers(0, 256, nbytes, dtype=np.uint8).view(st).reshape(vshape)
+    else:
+        kc, vc = np.zeros(kshape, st), np.zeros(vshape, st)
+    return WriteWorkload(name=name, key=key, value=value, slot_mapping=slots, k_cache=kc,
+                         v_cache=vc, in_dtype=in_dtype, kv_dtype=kv_dtype, k_scale=ks,
+                         v_scale=vs)
+
+
+def write_chunks(*, seed: int, chunk_lens, ctx_lens, num_blocks: int,
+                 block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Slot mapping of prefill chunks: chunk c appends chunk_lens[c] tokens
+    after ctx_lens[c] tokens of context, its sequence's blocks taken from a
+    random permutation of the pool (disjoint between chunks), so a chunk
+    starts mid-block whenever its context is not a multiple of the block size."""
+    rng = np.random.default_rng([seed, 9])
+    perm = rng.permutation(num_blocks)
+    slots, pos = [], 0
+    for n, ctx in zip(chunk_lens, ctx_lens):
+        nblk = -(-(int(ctx) + int(n)) // block_size)
+        table = perm[pos:pos + nblk]
+        pos += nblk
+        if pos > num_blocks:
+            raise ValueError("pool too small for the chunks")
+        t = np.arange(int(ctx), int(ctx) + int(n))
+        slots.append(table[t // block_size] * block_size + t % block_size)
+    return np.concatenate(slots).astype(np.int32) if slots else np.zeros(0, np.int32)
+
+
+def write_decode_step(*, seed: int, num_seqs: int, num_blocks: int,
+                      block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Slot mapping of one decode step: one new token per sequence, each in
+    its sequence's last block (distinct blocks), at a uniform offset."""
+    rng = np.random.default_rng([seed, 10])
+    blocks = rng.permutation(num_blocks)[:num_seqs]
+    if len(blocks) < num_seqs:
+        raise ValueError("pool too small for the sequences")
+    offs = rng.integers(0, block_size, num_seqs)
+    return (blocks * block_size + offs).astype(np.int32)
