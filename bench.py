@@ -12,7 +12,8 @@ every timed step a 1 GiB buffer is rewritten so no KV survives in the 256 MB
 Infinity Cache; step times come from HIP events on the launch stream.
 
 The other workloads (long-context split-KV, the mixed chunked-prefill step,
-fp8 KV) are timed the same way and reported under "per_config".  The
+fp8 KV, and the cache writes that precede attention) are timed the same way
+and reported under "per_config".  The
 CPU-baseline leg times the fp64 oracle on the host over the whole headline
 batch (single thread).
 
@@ -166,6 +167,64 @@ def time_prefill(torch, pa, d, wl, steps, warmup, flush):
     return [t.ms(i, 0, 1) for i in range(steps)]
 
 
+def write_cases(W):
+    """Cache writes of the decode and prefill steps above, and a long-context
+    fill: (label, WriteWorkload, pool blocks).  The caches are allocated on
+    the device (zeros); only the new rows and slot maps come from the host."""
+    cases = []
+    for label, seed, T, ind, kvd, nb in (("decode step, 64 seqs, bf16", 2, 64, "bf16", "bf16", 9216),
+                                         ("decode step, 256 seqs, bf16->fp8", 5, 256, "bf16", "fp8",
+                                          18432)):
+        slots = W.write_decode_step(seed=seed, num_seqs=T, num_blocks=nb)
+        cases.append((label, slots, ind, kvd, nb))
+    nb = 4 * (2048 + 512) // 16
+    cases.append(("4 prefill chunks of 512 after a 2048-token prefix, bf16",
+                  W.write_chunks(seed=4, chunk_lens=[512] * 4, ctx_lens=[2048] * 4, num_blocks=nb),
+                  "bf16", "bf16", nb))
+    for kvd in ("bf16", "fp8"):
+        cases.append((f"32768-token context fill, bf16->{kvd}",
+                       W.write_chunks(seed=6, chunk_lens=[32768], ctx_lens=[0], num_blocks=2048),
+                       "bf16", kvd, 2048))
+    out = []
+    for label, slots, ind, kvd, nb in cases:
+        wl = W.write_workload(seed=len(out) + 1, slot_mapping=slots, num_kv_heads=8, head_dim=128,
+                              in_dtype=ind, kv_dtype=kvd, num_blocks=nb, fill_cache=False,
+                              name=label)
+        out.append(wl)
+    return out
+
+
+def time_write(torch, pa, wl, steps, warmup, flush):
+    """Per-call ms of pa_write_kv on one write workload (caches on the device)."""
+    from workloads.device import dev
+    cdt = {"bf16": torch.bfloat16, "fp8": torch.uint8, "f32": torch.float32}[wl.kv_dtype]
+    kc = torch.zeros(wl.k_cache.shape, dtype=cdt, device="cuda")
+    vc = torch.zeros(wl.v_cache.shape, dtype=cdt, device="cuda")
+    key, value = dev(wl.key, wl.in_dtype), dev(wl.value, wl.in_dtype)
+    slots, ks, vs = dev(wl.slot_mapping), dev(wl.k_scale), dev(wl.v_scale)
+
+    def launch(ev):
+        ev[0].record()
+        pa.write_kv(key, value, kc, vc, slots, k_scale=ks, v_scale=vs)
+        ev[1].record()
+
+    wt = Timer(torch, warmup, 2)
+    for i in range(warmup):
+        flush.add_(1)
+        launch(wt.ev[i])
+    torch.cuda.synchronize()
+    t = Timer(torch, steps, 2)
+    for i in range(steps):
+        flush.add_(1)
+        launch(t.ev[i])
+    torch.cuda.synchronize()
+    ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
+    gbs = wl.bytes_moved() / ms / 1e6
+    return {"workload": wl.name, "tokens": wl.num_tokens, "ms": round(ms, 5),
+            "bytes": wl.bytes_moved(), "GBps": round(gbs, 2),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
 def med(xs):
     s = sorted(xs)
     return s[len(s) // 2]
@@ -207,6 +266,10 @@ def profile_one(args, W):
     import paged_kv_cache_22_amd as pa
     from workloads.device import Dev
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    if args.workload == "WRITE":
+        for wl in write_cases(W):
+            print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
+        return
     n = int(args.workload[1])
     res = {"workload": W.CONFIG_NAMES[n]}
     if n == 4:
@@ -235,9 +298,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5"],
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE"],
                     help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
-                         "plus the others under per_config)")
+                         "plus the others under per_config; WRITE = the cache writes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -302,6 +365,8 @@ def main():
                         "pairs": m.prefill.pairs(), "flops": m.prefill.flops(),
                         "tokens_attended_per_s": round(m.prefill.pairs() / pre_ms * 1e3, 1)},
         }
+        del dd, dp
+        per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
 
     kv = head["kv_GBps"]
     line = {

@@ -454,17 +454,29 @@ def write_workload(*, seed: int, slot_mapping, num_kv_heads: int, head_dim: int,
     """Rows N(0,1) (cast to bf16 for bf16 input); an fp8 cache gets the
     per-kv-head amax/448 scale of the rows drawn here.  ``fill_cache`` draws
     random bytes for the initial cache, else zeros."""
-    rng = np.random.default_rng([seed, 7])
     slots = np.asarray(slot_mapping, dtype=np.int32)
     T = len(slots)
     shape = (T, num_kv_heads, head_dim)
-    k32 = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
-    v32 = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    # rows drawn in chunks of 1024 tokens, chunk k of K from default_rng([seed, 7, 1, k])
+    # and of V from default_rng([seed, 7, 2, k]), on a thread pool
+    k32 = np.empty(shape, np.float32)
+    v32 = np.empty(shape, np.float32)
+    row = num_kv_heads * head_dim
+
+    def draw(job):
+        which, k = job
+        t0, t1 = k * 1024, min(T, (k + 1) * 1024)
+        dst = k32 if which == 1 else v32
+        r = np.random.default_rng([seed, 7, which, k])
+        dst[t0:t1] = r.standard_normal((t1 - t0) * row, dtype=np.float32).reshape(t1 - t0, *shape[1:])
+
+    jobs = [(w, k) for w in (1, 2) for k in range(-(-T // 1024))]
+    with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+        list(ex.map(draw, jobs))
     if in_dtype == "bf16":
         key, value = to_bf16_bits(k32), to_bf16_bits(v32)
-        kf = key.astype(np.uint32) << 16
-        vf = value.astype(np.uint32) << 16
-        kf, vf = kf.view(np.float32), vf.view(np.float32)
+        kf = (key.astype(np.uint32) << 16).view(np.float32)
+        vf = (value.astype(np.uint32) << 16).view(np.float32)
     else:
         key, value, kf, vf = k32, v32, k32, v32
     ks = vs = None
