@@ -8,8 +8,10 @@ kv-heads, head_dim 128, block_size 16, lengths uniform in [512, 4096] (seed
 the decode path over that batch: pa_decode (the split-KV partition kernel,
 then the log-sum-exp merge for sequences with several partitions), inputs
 resident in HBM.  Before
-every timed step a 1 GiB buffer is rewritten so no KV survives in the 256 MB
-Infinity Cache; step times come from HIP events on the launch stream.
+every timed step a 1 GiB buffer is read (a reduction into one scalar) so no
+input survives in the L2 or the 256 MB Infinity Cache; a read leaves clean
+lines behind, so no write-back of the flush lands inside the next timed
+kernel.  Step times come from HIP events on the launch stream.
 
 The other workloads (long-context split-KV, the mixed chunked-prefill step,
 fp8 KV, and the cache writes that precede attention) are timed the same way
@@ -80,6 +82,20 @@ def cpu_baseline(wl):
                       f"all {wl.num_kv_heads} kv-heads (fp64 numpy oracle, 1 thread)"}
 
 
+class CacheFlush:
+    """Evicts the caches between timed steps by reading a 1 GiB buffer.
+    Reading (not rewriting) leaves no dirty lines whose write-back would be
+    charged to the next kernel."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.out = torch.zeros((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=(0,), out=self.out)
+
+
 class Timer:
     """Per-step HIP events on the current stream, around each launch group."""
 
@@ -106,12 +122,12 @@ def time_decode(torch, pa, d, wl, P, steps, warmup, flush):
 
     wt = Timer(torch, warmup, 2)
     for i in range(warmup):
-        flush.add_(1)
+        flush()
         launch(wt.ev[i])
     torch.cuda.synchronize()
     t = Timer(torch, steps, 2)
     for i in range(steps):
-        flush.add_(1)
+        flush()
         launch(t.ev[i])
     torch.cuda.synchronize()
     ms = [t.ms(i, 0, 1) for i in range(steps)]
@@ -134,12 +150,12 @@ def time_partition_kernel(torch, pa, d, wl, P, steps, warmup, flush):
         ev[1].record()
 
     for i in range(warmup):
-        flush.add_(1)
+        flush()
         launch(Timer(torch, 1, 2).ev[0])
     torch.cuda.synchronize()
     t = Timer(torch, steps, 2)
     for i in range(steps):
-        flush.add_(1)
+        flush()
         launch(t.ev[i])
     torch.cuda.synchronize()
     return [t.ms(i, 0, 1) for i in range(steps)]
@@ -156,12 +172,12 @@ def time_prefill(torch, pa, d, wl, steps, warmup, flush):
 
     wt = Timer(torch, warmup, 2)
     for i in range(warmup):
-        flush.add_(1)
+        flush()
         launch(wt.ev[i])
     torch.cuda.synchronize()
     t = Timer(torch, steps, 2)
     for i in range(steps):
-        flush.add_(1)
+        flush()
         launch(t.ev[i])
     torch.cuda.synchronize()
     return [t.ms(i, 0, 1) for i in range(steps)]
@@ -210,12 +226,12 @@ def time_write(torch, pa, wl, steps, warmup, flush):
 
     wt = Timer(torch, warmup, 2)
     for i in range(warmup):
-        flush.add_(1)
+        flush()
         launch(wt.ev[i])
     torch.cuda.synchronize()
     t = Timer(torch, steps, 2)
     for i in range(steps):
-        flush.add_(1)
+        flush()
         launch(t.ev[i])
     torch.cuda.synchronize()
     ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
@@ -265,7 +281,7 @@ def profile_one(args, W):
     import torch
     import paged_kv_cache_22_amd as pa
     from workloads.device import Dev
-    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = CacheFlush(torch)
     if args.workload == "WRITE":
         for wl in write_cases(W):
             print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
@@ -325,7 +341,7 @@ def main():
     from workloads.device import Dev
 
     torch.cuda.init()
-    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = CacheFlush(torch)
     d = Dev(wl)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

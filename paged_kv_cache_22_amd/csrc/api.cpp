@@ -317,7 +317,10 @@ int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype, const void* key, con
         (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
         return PA_ERR_ALIGN;
     const int chunk = kv_dtype == PA_FP8_E4M3 ? 16 : kv_dtype == PA_BF16 ? 8 : 4;
-    if (((long long)num_kv_heads * (head_dim / chunk) + 3) / 4 > kMaxGridY) return PA_ERR_SHAPE;
+    // one workgroup per (16 tokens, 16 chunk slots) at the least: the 1-D grid must fit
+    if (((long long)num_tokens + 15) / 16 * (((long long)num_kv_heads * (head_dim / chunk) + 15) / 16) >
+        0x7fffffffLL)
+        return PA_ERR_SHAPE;
     if (num_tokens == 0) return PA_OK;
     pa::WriteArgs a{};
     a.k_cache = k_cache;

@@ -5,47 +5,45 @@
 // 四: the cache is addressed through block tables, so a new token's position
 // is a (block, offset) pair).
 //
-// One lane per (token, kv-head, 16-byte K chunk).  Lanes of a wave take 64
-// consecutive tokens of one (kv-head, chunk): the new tokens of a prefill
-// chunk occupy consecutive offsets of a block, so 16 neighbouring lanes fill
-// one 256-byte K chunk run and whole 16-token V rows, and the stores
-// coalesce.  A decode step writes one token per sequence into unrelated
-// blocks: those stores are scattered whatever the mapping, and the call is
-// dominated by launch latency.
+// Lane map.  A lane handles one 16-byte K chunk (X dims) of one kv-head for
+// TPL tokens (1, 2 or 4: about 128 input bytes per lane, so each wave keeps
+// many loads in flight).  A wave is 16 tokens x 4 (kv-head, chunk) slots,
+// the slots consecutive in a token's row: each load instruction reads
+// 64-byte runs of 16 token rows.  The new tokens of a prefill chunk occupy
+// consecutive offsets of a block, so the 16 tokens of a K store fill one
+// 256-byte chunk run and each V store one 16-token V row.  A decode step
+// writes one token per sequence into unrelated blocks: those stores scatter
+// whatever the map, and the call is dominated by launch latency.
 #include "device.h"
 #include "launch.h"
 
 namespace pa {
 namespace {
 
-constexpr int kTokensPerWave = 64;
-constexpr int kWavesPerGroup = 4;
+constexpr int kWaves = 4;
 constexpr int kBlock = 16;
 
 // cache elements per 16-byte K chunk
 template <int KV>
 constexpr int chunk_elems() { return KV == KV_FP8 ? 16 : KV == KV_BF16 ? 8 : 4; }
 
-// X input values -> fp32
+// one input row piece (X values in 16-byte pieces) -> fp32
 template <int IN, int X>
-__device__ __forceinline__ void load_row(const char* p, float (&x)[X]) {
+__device__ __forceinline__ void unpack_row(const u32x4 (&w)[X * (IN == KV_BF16 ? 2 : 4) / 16],
+                                           float (&x)[X]) {
     if constexpr (IN == KV_BF16) {
 #pragma unroll
-        for (int c = 0; c < X / 8; ++c) {
-            const u32x4 w = ld16(p + 16 * c);
+        for (int c = 0; c < X / 8; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[8 * c + 2 * i] = bf16_lo(w[i]);
-                x[8 * c + 2 * i + 1] = bf16_hi(w[i]);
+                x[8 * c + 2 * i] = bf16_lo(w[c][i]);
+                x[8 * c + 2 * i + 1] = bf16_hi(w[c][i]);
             }
-        }
     } else {
 #pragma unroll
-        for (int c = 0; c < X / 4; ++c) {
-            const u32x4 w = ld16(p + 16 * c);
+        for (int c = 0; c < X / 4; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[4 * c + i] = __uint_as_float(w[i]);
-        }
+            for (int i = 0; i < 4; ++i) x[4 * c + i] = __uint_as_float(w[c][i]);
     }
 }
 
@@ -61,81 +59,178 @@ __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float 
     return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// most tokens per lane: about 128 input bytes (K and V) in flight per lane
 template <int IN, int KV>
-__global__ __launch_bounds__(kTokensPerWave* kWavesPerGroup) void write_kv_kernel(const WriteArgs a) {
+constexpr int max_tokens_per_lane() {
+    return 64 / (chunk_elems<KV>() * (IN == KV_BF16 ? 2 : 4));
+}
+
+// The V rows of one wave's transposed region, read back from the staged
+// chunks: lane L stores bytes [16L, 16L + 16) of the 1 KiB region that the
+// wave's four chunks cover in a whole 16-token block (rows of 16 tokens,
+// dim-major).  Staged entry c*16 + r holds chunk c (16 bytes) of token r.
+template <int KV>
+__device__ __forceinline__ u32x4 transposed_v(const uint8_t* st, int L) {
+    const int c = L >> 4;
+    u32x4 o;
+    if constexpr (KV == KV_BF16) {          // row = 16 tokens x 2 B: lane -> half a row
+        const int e = (L >> 1) & 7, t0 = 8 * (L & 1);
+        const uint8_t* p = st + (c * 16 + t0) * 16 + 2 * e;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            o[m] = (unsigned)*reinterpret_cast<const uint16_t*>(p + (2 * m) * 16) |
+                   ((unsigned)*reinterpret_cast<const uint16_t*>(p + (2 * m + 1) * 16) << 16);
+    } else if constexpr (KV == KV_FP8) {    // row = 16 tokens x 1 B: lane -> one row
+        const int e = L & 15;
+        const uint8_t* p = st + c * 16 * 16 + e;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            o[m] = (unsigned)p[(4 * m) * 16] | ((unsigned)p[(4 * m + 1) * 16] << 8) |
+                   ((unsigned)p[(4 * m + 2) * 16] << 16) | ((unsigned)p[(4 * m + 3) * 16] << 24);
+    } else {                                // row = 16 tokens x 4 B: lane -> a quarter row
+        const int e = (L >> 2) & 3, t0 = 4 * (L & 3);
+        const uint8_t* p = st + (c * 16 + t0) * 16 + 4 * e;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) o[m] = *reinterpret_cast<const unsigned*>(p + m * 16);
+    }
+    return o;
+}
+
+template <int IN, int KV, int TPL>
+__global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a) {
     constexpr int X = chunk_elems<KV>();
     constexpr int kInBytes = IN == KV_BF16 ? 2 : 4;
     constexpr int kCacheBytes = KV == KV_FP8 ? 1 : KV == KV_BF16 ? 2 : 4;
-    const int t = blockIdx.x * kTokensPerWave + threadIdx.x;
-    const int hc = blockIdx.y * kWavesPerGroup + threadIdx.y;
+    constexpr int kPieces = X * kInBytes / 16;                 // 16-byte input loads per row
+    __shared__ u32x4 stage[kWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r = lane & 15;
+    // 1-D grid, chunk-slot groups fastest: neighbouring workgroups take the
+    // neighbouring (kv-head, chunk) slots of the same tokens, whose cache
+    // tiles and input bytes are adjacent in memory
+    const int slot_groups = (a.num_kv_heads * (a.head_dim / X) + 4 * kWaves - 1) / (4 * kWaves);
+    const int tg = blockIdx.x / slot_groups;
+    const int hc0 = (blockIdx.x - tg * slot_groups) * (4 * kWaves) + w * 4;   // the wave's first slot
+    const int hc = hc0 + (lane >> 4);
     const int d = a.head_dim;
     const int nchunk = d / X;
-    if (t >= a.num_tokens || hc >= a.num_kv_heads * nchunk) return;
-    const int slot = a.slot_mapping[t];
-    if (slot < 0 || slot >= a.num_blocks * kBlock) return;   // padding / outside the pool
+    // rows and nchunk are multiples of 4, so a wave's four slots are all
+    // valid or all past the end (the return is wave-uniform) and share a head
+    if (hc >= a.num_kv_heads * nchunk) return;
     const int h = hc / nchunk;
     const int j = hc - h * nchunk;
-    const int blk = slot / kBlock;
-    const int off = slot - blk * kBlock;
-    const size_t tile = (size_t)blk * a.num_kv_heads + h;   // (block, kv-head) tile
+    const int tbase = tg * (16 * TPL) + r;
+    const int cap = a.num_blocks * kBlock;
 
-    const char* ksrc = static_cast<const char*>(a.key) +
-                       ((size_t)t * a.key_stride + (size_t)h * d + (size_t)j * X) * kInBytes;
-    const char* vsrc = static_cast<const char*>(a.value) +
-                       ((size_t)t * a.value_stride + (size_t)h * d + (size_t)j * X) * kInBytes;
-    float kx[X], vx[X];
-    load_row<IN, X>(ksrc, kx);
-    load_row<IN, X>(vsrc, vx);
-
-    // K: chunk j of the tile, 16 bytes at token offset `off`
-    char* kdst = static_cast<char*>(a.k_cache) + ((tile * nchunk + j) * kBlock + off) * 16;
-    // V: dims j*X .. j*X+X-1 of the tile, one element per dim row at `off`
-    char* vdst = static_cast<char*>(a.v_cache) + ((tile * d + (size_t)j * X) * kBlock + off) * kCacheBytes;
-
-    if constexpr (KV == KV_FP8) {
-        const float ks = a.k_scale[h];
-        const float vs = a.v_scale[h];
-        u32x4 kw;
+    // All loads first and unconditionally, so that they are all in flight
+    // together: a token past the end reads the last token's row (always
+    // valid memory) and is dropped at the store.
+    int slot[TPL];
+    u32x4 kraw[TPL][kPieces], vraw[TPL][kPieces];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            kw[i] = pack_fp8x4(to_e4m3_range(kx[4 * i], ks), to_e4m3_range(kx[4 * i + 1], ks),
-                               to_e4m3_range(kx[4 * i + 2], ks), to_e4m3_range(kx[4 * i + 3], ks));
-        *reinterpret_cast<u32x4*>(kdst) = kw;
+    for (int i = 0; i < TPL; ++i) {
+        const int t = min(tbase + 16 * i, a.num_tokens - 1);
+        slot[i] = a.slot_mapping[t];
+        if (tbase + 16 * i >= a.num_tokens) slot[i] = -1;
+    }
 #pragma unroll
-        for (int i = 0; i < X / 4; ++i) {
-            const unsigned w = pack_fp8x4(to_e4m3_range(vx[4 * i], vs), to_e4m3_range(vx[4 * i + 1], vs),
-                                          to_e4m3_range(vx[4 * i + 2], vs), to_e4m3_range(vx[4 * i + 3], vs));
+    for (int i = 0; i < TPL; ++i) {
+        const int t = min(tbase + 16 * i, a.num_tokens - 1);
+        const char* ks = static_cast<const char*>(a.key) +
+                         ((size_t)t * a.key_stride + (size_t)h * d + (size_t)j * X) * kInBytes;
+        const char* vs = static_cast<const char*>(a.value) +
+                         ((size_t)t * a.value_stride + (size_t)h * d + (size_t)j * X) * kInBytes;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                reinterpret_cast<uint8_t*>(vdst)[(4 * i + e) * kBlock] = (uint8_t)(w >> (8 * e));
+        for (int p = 0; p < kPieces; ++p) {
+            kraw[i][p] = ld16(ks + 16 * p);
+            vraw[i][p] = ld16(vs + 16 * p);
         }
-    } else if constexpr (KV == KV_BF16) {
-        u32x4 kw;
+    }
+
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kw[i] = (__float_as_uint(kx[2 * i]) >> 16) | (__float_as_uint(kx[2 * i + 1]) & 0xffff0000u);
-        *reinterpret_cast<u32x4*>(kdst) = kw;
+    for (int i = 0; i < TPL; ++i) {
+        const bool live = slot[i] >= 0 && slot[i] < cap;       // not padding, inside the pool
+        // Wave-uniform: are the wave's 16 tokens one whole block, in order?
+        // (lane 0 holds token r = 0; every lane group holds the same tokens)
+        const int s0 = __builtin_amdgcn_readfirstlane(slot[i]);
+        const bool whole = __all(live && slot[i] == s0 + r) && (s0 % kBlock) == 0;
+
+        // this token's K chunk and V elements, in cache encoding
+        u32x4 kw, vw;
+        if constexpr (KV == KV_FP8) {
+            float kx[X], vx[X];
+            unpack_row<IN, X>(kraw[i], kx);
+            unpack_row<IN, X>(vraw[i], vx);
+            const float ksc = a.k_scale[h];
+            const float vsc = a.v_scale[h];
 #pragma unroll
-        for (int i = 0; i < X; ++i)
-            reinterpret_cast<uint16_t*>(vdst)[i * kBlock] = (uint16_t)(__float_as_uint(vx[i]) >> 16);
-    } else {
-        u32x4 kw;
+            for (int q = 0; q < 4; ++q) {
+                kw[q] = pack_fp8x4(to_e4m3_range(kx[4 * q], ksc), to_e4m3_range(kx[4 * q + 1], ksc),
+                                   to_e4m3_range(kx[4 * q + 2], ksc), to_e4m3_range(kx[4 * q + 3], ksc));
+                vw[q] = pack_fp8x4(to_e4m3_range(vx[4 * q], vsc), to_e4m3_range(vx[4 * q + 1], vsc),
+                                   to_e4m3_range(vx[4 * q + 2], vsc), to_e4m3_range(vx[4 * q + 3], vsc));
+            }
+        } else {
+            // bf16 / fp32: the input bits themselves (no arithmetic)
+            kw = kraw[i][0];
+            vw = vraw[i][0];
+        }
+        const int blk = slot[i] / kBlock;
+        const int off = slot[i] - blk * kBlock;
+        const size_t tile = (size_t)blk * a.num_kv_heads + h;    // (block, kv-head) tile
+        // K: chunk j of the tile, 16 bytes at token offset `off`
+        if (live)
+            *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) +
+                                      ((tile * nchunk + j) * kBlock + off) * 16) = kw;
+        if (whole) {
+            // V through LDS: the wave's four chunks of the 16 tokens cover the
+            // 1 KiB run of dim rows (hc0's first dim .. +4X) of this block's tile
+            stage[w][lane] = vw;
+            __builtin_amdgcn_wave_barrier();
+            const u32x4 o = transposed_v<KV>(reinterpret_cast<const uint8_t*>(stage[w]), lane);
+            __builtin_amdgcn_wave_barrier();
+            const int j0 = (hc0 - h * nchunk);
+            char* vreg = static_cast<char*>(a.v_cache) + (tile * d + (size_t)j0 * X) * kBlock * kCacheBytes;
+            *reinterpret_cast<u32x4*>(vreg + 16 * lane) = o;
+        } else if (live) {
+            // V: dims j*X .. j*X+X-1 of the tile, one element per dim row at `off`
+            char* vdst = static_cast<char*>(a.v_cache) +
+                         ((tile * d + (size_t)j * X) * kBlock + off) * kCacheBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kw[i] = __float_as_uint(kx[i]);
-        *reinterpret_cast<u32x4*>(kdst) = kw;
-#pragma unroll
-        for (int i = 0; i < X; ++i) reinterpret_cast<float*>(vdst)[i * kBlock] = vx[i];
+            for (int e = 0; e < X; ++e) {
+                if constexpr (KV == KV_FP8)
+                    reinterpret_cast<uint8_t*>(vdst)[e * kBlock] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
+                else if constexpr (KV == KV_BF16)
+                    reinterpret_cast<uint16_t*>(vdst)[e * kBlock] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+                else
+                    reinterpret_cast<unsigned*>(vdst)[e * kBlock] = vw[e];
+            }
+        }
     }
 }
+
+template <int IN, int KV, int TPL>
+hipError_t launch_tpl(const WriteArgs& a, hipStream_t s, long long slot_groups) {
+    const long long groups = ((long long)a.num_tokens + 16 * TPL - 1) / (16 * TPL) * slot_groups;
+    hipLaunchKernelGGL((write_kv_kernel<IN, KV, TPL>), dim3((unsigned)groups), dim3(64 * kWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+// Several tokens per lane keep more bytes in flight per wave, one token per
+// lane gives more workgroups: take the most tokens per lane that still
+// leaves at least kMinGroups workgroups (8 per CU).
+constexpr long long kMinGroups = 2048;
 
 template <int IN, int KV>
 hipError_t launch_t(const WriteArgs& a, hipStream_t s) {
     constexpr int X = chunk_elems<KV>();
-    const int rows = a.num_kv_heads * (a.head_dim / X);
-    dim3 grid((a.num_tokens + kTokensPerWave - 1) / kTokensPerWave,
-              (rows + kWavesPerGroup - 1) / kWavesPerGroup);
-    dim3 block(kTokensPerWave, kWavesPerGroup);
-    hipLaunchKernelGGL((write_kv_kernel<IN, KV>), grid, block, 0, s, a);
-    return hipGetLastError();
+    constexpr int kMax = max_tokens_per_lane<IN, KV>();
+    const long long rows = (long long)a.num_kv_heads * (a.head_dim / X);
+    const long long slot_groups = (rows + 4 * kWaves - 1) / (4 * kWaves);
+    const long long groups_max = ((long long)a.num_tokens + 16 * kMax - 1) / (16 * kMax) * slot_groups;
+    if (kMax > 1 && groups_max >= kMinGroups) return launch_tpl<IN, KV, kMax>(a, s, slot_groups);
+    return launch_tpl<IN, KV, 1>(a, s, slot_groups);
 }
 
 }  // namespace

@@ -91,6 +91,25 @@ def test_write_matches_oracle(in_dtype, kv_dtype, hkv, d):
     assert_same(vc, ev, f"{wl.name} V")
 
 
+@pytest.mark.parametrize("in_dtype,kv_dtype", DTYPES)
+@pytest.mark.parametrize("hkv,d", [(8, 128), (10, 64)])
+def test_whole_blocks_and_partial_groups(in_dtype, kv_dtype, hkv, d):
+    """Token groups that fill whole blocks in order (chunks starting on a
+    block boundary) next to groups that straddle blocks or end early, and a
+    whole-looking group broken by one padding token."""
+    nb = 80
+    slots = W.write_chunks(seed=70 + d, chunk_lens=[64, 32, 40, 7, 48], ctx_lens=[0, 16, 3, 32, 0],
+                           num_blocks=nb)
+    slots[-20] = -1                       # inside the last chunk's second block
+    wl = W.write_workload(seed=8, slot_mapping=slots, num_kv_heads=hkv, head_dim=d,
+                          in_dtype=in_dtype, kv_dtype=kv_dtype, num_blocks=nb,
+                          name=f"whole blocks {in_dtype}->{kv_dtype}")
+    kc, vc = run(wl)
+    ek, ev = expected(wl)
+    assert_same(kc, ek, f"{wl.name} K")
+    assert_same(vc, ev, f"{wl.name} V")
+
+
 def ties_workload(in_dtype):
     """Scale 1: inputs are every e4m3 value, every midpoint between two
     neighbours (the ties), values past 448 and the negatives of all of them."""
@@ -194,18 +213,32 @@ def test_fp8_decode_step_full_size():
     assert_same(vc, ev, "decode step V")
 
 
-def test_fp8_bulk_fill_sampled():
-    """A 32768-token context written into an fp8 cache in one call; the
-    oracle writes every 16th token (a sample spread over all blocks) and
-    those slots are compared byte for byte."""
-    nb = 2048
-    slots = W.write_chunks(seed=60, chunk_lens=[32768], ctx_lens=[0], num_blocks=nb)
-    wl = W.write_workload(seed=60, slot_mapping=slots, num_kv_heads=8, head_dim=128,
-                          in_dtype="bf16", kv_dtype="fp8", num_blocks=nb, fill_cache=False,
-                          name="fill 32768 fp8")
+@pytest.mark.parametrize("in_dtype,kv_dtype,hkv,d,T", [
+    ("bf16", "fp8", 8, 128, 32768),      # the context-fill workload the benchmark times
+    ("bf16", "bf16", 8, 128, 32768),
+    ("f32", "f32", 2, 64, 65536),
+])
+def test_large_fill_sampled(in_dtype, kv_dtype, hkv, d, T):
+    """Large writes, where each lane handles several tokens: one long chunk
+    from a block boundary, a second one starting mid-block and a few padding
+    tokens.  The oracle writes a sample of 2048 tokens spread over the whole
+    call (one in every T/2048), and those slots are compared byte for byte."""
+    nb = -(-T // 16) + 8
+    slots = W.write_chunks(seed=60 + d, chunk_lens=[T - 100, 100], ctx_lens=[0, 5], num_blocks=nb)
+    slots[[7, T // 2, T - 3]] = -1
+    wl = W.write_workload(seed=60, slot_mapping=slots, num_kv_heads=hkv, head_dim=d,
+                          in_dtype=in_dtype, kv_dtype=kv_dtype, num_blocks=nb, fill_cache=False,
+                          name=f"fill {T} {in_dtype}->{kv_dtype}")
     kc, vc = run(wl)
-    sample = np.arange(0, 32768, 16) + np.random.default_rng(60).integers(0, 16, 2048)
+    step = T // 2048
+    sample = np.arange(0, T, step) + np.random.default_rng(60).integers(0, step, 2048)
+    sample = np.union1d(sample, [7, T - 100, T - 97, T - 1])      # padding, second chunk
     ek, ev = expected(wl, tokens=sample)
-    blk, off = slots[sample] // 16, slots[sample] % 16
+    live = sample[slots[sample] >= 0]
+    blk, off = slots[live] // 16, slots[live] % 16
     assert_same(kc[blk, :, :, off, :], ek[blk, :, :, off, :], "fill K (sample)")
     assert_same(vc[blk, :, :, off], ev[blk, :, :, off], "fill V (sample)")
+    # the padding tokens' slots were never written: zeros from the initial cache
+    untouched = np.setdiff1d(np.arange(nb * 16), slots[slots >= 0])
+    ub, uo = untouched // 16, untouched % 16
+    assert not kc[ub, :, :, uo, :].any() and not vc[ub, :, :, uo].any()
