@@ -123,6 +123,33 @@ int pa_decode(void* out, const void* q, int q_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-query decode: each sequence has q_len queries, the newest q_len
+ * tokens already in its cache, as when drafted tokens are verified in one
+ * step (speculative decoding: in vllm-mblt 0.8.0, "Serve an EAGLE-3 Model",
+ * the base model verifies each round's drafted tokens).  Query i of sequence b sits at position L - q_len + i
+ * (L = seq_lens[b]) and attends to keys 0 .. L - q_len + i: the causal mask
+ * of a prefill chunk whose context is L - q_len.
+ *
+ * q, out  [num_seqs, q_len, num_q_heads, head_dim] (out in q's dtype).
+ * q_len = 1 is pa_decode.  With q_len * G <= 16 the (query, head) pairs share
+ * one pass over each sequence's K/V (the decode kernel, split-KV and merge as
+ * in pa_decode); the workspace is then
+ * pa_decode_workspace_size(num_seqs, q_len * num_q_heads, head_dim,
+ * max_seq_len, partition_size) bytes.  With q_len * G > 16 the prefill-chunk
+ * kernel runs each sequence as one chunk (partition_size and workspace are
+ * ignored).  A sequence with seq_len 0 gets zero rows; 0 < seq_len < q_len
+ * breaks the contract (its rows are unspecified).
+ */
+int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len,
+                          const void* k_cache, const void* v_cache, int kv_dtype,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, const float* k_scale,
+                          const float* v_scale, int partition_size, int max_seq_len,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-KV decode, partition kernel only: writes partial_out / partial_lse
  * for every partition of every sequence (partitions past ceil(L / P) are not
  * written and must not be read; pa_merge_partitions ignores them).
@@ -161,7 +188,8 @@ int pa_merge_partitions(void* out, int out_dtype, float* out_lse,
  * bottom-right of the score matrix).  Several block-table rows may reference
  * the same physical blocks (a shared prefix).  max_q_len is the host-side
  * bound on every chunk's length; it sizes the grid.  out_lse (fp32
- * [total_q, num_q_heads], natural log) may be NULL.
+ * [total_q, num_q_heads], natural log) may be NULL.  A chunk whose seq_len is
+ * below its q_len has no context for its rows: they get zeros (lse -inf).
  */
 int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
                      const int32_t* cu_q_lens, int total_q, int max_q_len,

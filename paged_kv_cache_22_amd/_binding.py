@@ -25,6 +25,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f,
                        _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "pa_decode_multi_query": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
+                                   _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i,
                                   _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "pa_merge_partitions": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -145,6 +147,36 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
                        int(partition_size), int(max_seq_len),
                        _dev(workspace, "workspace"), ws_bytes, _stream(q))
     _check("pa_decode", st)
+    return out
+
+
+def decode_multi_query(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
+                       scale: Optional[float] = None, partition_size: int = 0, k_scale=None,
+                       v_scale=None, out=None, workspace=None):
+    """Multi-query decode (pa_decode_multi_query): q [B, q_len, Hq, d], the
+    newest q_len cached tokens of each sequence, causal among themselves.
+    Returns out with q's shape and dtype."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q_len, Hq, d]")
+    B, qn, Hq, d = q.shape
+    _, _, _, NB, Hkv, bs = _kv_dims(q.reshape(B, qn * Hq, d), k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = d ** -0.5
+    ws_need = decode_workspace_size(B, qn * Hq, d, max_seq_len, partition_size)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_multi_query(_dev(out, "out"), _dev(q, "q"), _dtype_code(q, False), qn,
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dtype_code(k_cache, True), _dev(block_table, "block_table"),
+                                   block_table.shape[1], _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d,
+                                   bs, NB, float(scale), _dev(k_scale, "k_scale"),
+                                   _dev(v_scale, "v_scale"), int(partition_size), int(max_seq_len),
+                                   _dev(workspace, "workspace"), ws_bytes, _stream(q))
+    _check("pa_decode_multi_query", st)
     return out
 
 

@@ -92,6 +92,7 @@ pa::DecodeArgs make_decode_args(const void* q, int q_dtype, const void* k_cache,
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
     a.scale = scale;
+    a.q_len = 1;
     a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
     a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
     return a;
@@ -186,21 +187,23 @@ int pa_merge_partitions(void* out, int out_dtype, float* out_lse, const float* p
     return hip_status(pa::launch_merge(m, stream));
 }
 
-int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
-              int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
-              const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-              int block_size, int num_blocks, float scale, const float* k_scale,
-              const float* v_scale, int partition_size, int max_seq_len, void* workspace,
-              size_t workspace_bytes, void* stream) {
-    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
-                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
-    if (st != PA_OK) return st;
-    if (num_seqs > 0 && !out) return PA_ERR_NULL;
-    if (!aligned16(out)) return PA_ERR_ALIGN;
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_multi_query with q_len * G <= 16: the decode kernel
+// (columns = (query, head) pairs), split-KV partials merged when P > 0
+int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
+                const void* v_cache, int kv_dtype, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, float scale, const float* k_scale,
+                const float* v_scale, int partition_size, int max_seq_len, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    const int rows_per_seq = q_len * num_q_heads;   // output rows of one sequence
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
                                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
                                         num_kv_heads, head_dim, scale, k_scale, v_scale);
+    a.q_len = q_len;
     if (partition_size == 0) {
         if (num_seqs == 0) return PA_OK;
         a.out = out;
@@ -208,7 +211,7 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
         a.grid_parts = 1;
         return hip_status(pa::launch_decode(a, stream));
     }
-    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+    const size_t need = pa_decode_workspace_size(num_seqs, rows_per_seq, head_dim, max_seq_len,
                                                  partition_size);
     if (num_seqs > 0 && need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
@@ -221,7 +224,7 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
         return hip_status(pa::launch_decode(a, stream));
     }
     // workspace: partial outputs | partial lse
-    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    const size_t rows = (size_t)num_seqs * rows_per_seq * parts;
     char* ws = reinterpret_cast<char*>(workspace);
     const size_t off_lse = round_up(rows * head_dim * sizeof(float), kRegionAlign);
     a.out = out;
@@ -229,9 +232,9 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
     a.part_lse = reinterpret_cast<float*>(ws + off_lse);
     a.single_direct = 1;
     a.max_parts = parts;
-    a.partition_blocks = partition_size / block_size;
+    a.partition_blocks = partition_size / kBlockSize;
     a.grid_parts = parts;
-    st = hip_status(pa::launch_decode(a, stream));
+    int st = hip_status(pa::launch_decode(a, stream));
     if (st != PA_OK) return st;
     pa::MergeArgs m{};
     m.out = out;
@@ -243,10 +246,82 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
     m.partition_size = partition_size;
     m.max_parts = parts;
     m.num_seqs = num_seqs;
-    m.num_q_heads = num_q_heads;
+    m.num_q_heads = rows_per_seq;
     m.head_dim = head_dim;
     m.skip_single = 1;
     return hip_status(pa::launch_merge(m, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+              int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
+              const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, float scale, const float* k_scale,
+              const float* v_scale, int partition_size, int max_seq_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    return decode_impl(out, q, q_dtype, 1, k_cache, v_cache, kv_dtype, block_table,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
+                          const void* v_cache, int kv_dtype, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                          int partition_size, int max_seq_len, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (q_len <= 0) return PA_ERR_SHAPE;
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    if ((long long)num_seqs * q_len * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const int G = num_q_heads / num_kv_heads;
+    if ((long long)q_len * G <= kMaxGroup)
+        return decode_impl(out, q, q_dtype, q_len, k_cache, v_cache, kv_dtype, block_table,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                           head_dim, scale, k_scale, v_scale, partition_size, max_seq_len,
+                           workspace, workspace_bytes, stream);
+    // more (query, head) pairs than MFMA columns: the prefill kernel, each
+    // sequence a chunk of q_len rows (no partitions, no workspace)
+    if (((long long)q_len * G + 127) / 128 > kMaxGridY) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    pa::PrefillArgs a{};
+    a.out = out;
+    a.out_lse = nullptr;
+    a.q = q;
+    a.cu_q_lens = nullptr;
+    a.uniform_q_len = q_len;
+    a.total_q = num_seqs * q_len;
+    a.max_q_len = q_len;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.num_chunks = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale = scale;
+    return hip_status(pa::launch_prefill(a, stream));
 }
 
 int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, const int32_t* cu_q_lens,

@@ -28,6 +28,14 @@
 //     are non-temporal (each tile is read once).
 // Split-KV: partition p covers blocks [p*PB, (p+1)*PB); it writes its
 // normalised output and lse (natural log) for the log-sum-exp merge.
+//
+// Several queries per sequence (MQ): the q_len newest cached tokens are all
+// queries, as when a batch of drafted tokens is verified in one step.  Query
+// i sits at position L - q_len + i and sees keys 0 .. L - q_len + i.  With
+// q_len * G <= 16 the (query, head) pairs fill the 16 MFMA columns, column
+// r = i * G + g, so verifying q_len tokens reads the sequence's K/V once,
+// like a single decode step; each column carries its own causal limit into
+// the score mask of the last blocks.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -35,7 +43,7 @@
 namespace pa {
 namespace {
 
-template <int D, int KIND, bool SPLIT, int WAVES>
+template <int D, int KIND, bool SPLIT, bool MQ, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
@@ -52,12 +60,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     const int nblk = (L + kBS - 1) / kBS;
     const int pb = SPLIT ? a.partition_blocks : nblk;
     const int j0 = part * pb;
-    const int qh = h * G + r;
-    const bool col_ok = r < G;
+    // column r: query qi (0 without MQ), q-head qh; its output / q row
+    const int qn = MQ ? a.q_len : 1;
+    const int qi = MQ ? r / G : 0;
+    const int qh = h * G + (MQ ? r - qi * G : r);
+    const bool col_ok = r < qn * G;
+    const size_t row = ((size_t)b * qn + qi) * Hq + qh;
+    // keys this column sees: 0 .. lim-1 (L without MQ)
+    const int lim = L - qn + 1 + qi;
+    const int lim_min = L - qn + 1;  // the smallest limit of the sequence's columns
 
     if (j0 >= nblk) {  // uniform over the workgroup
         if (!SPLIT && w == 0 && col_ok) {  // empty sequence: zeros
-            QT* o = reinterpret_cast<QT*>(a.out) + ((size_t)b * Hq + qh) * D;
+            QT* o = reinterpret_cast<QT*>(a.out) + row * D;
 #pragma unroll
             for (int n = 0; n < NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
         }
@@ -68,7 +83,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     const int n_mine = max(0, (j1 - j0 - w + WAVES - 1) / WAVES);
 
     typename T::QOp Q;
-    T::load_q(Q, col_ok ? reinterpret_cast<const QT*>(a.q) + ((size_t)b * Hq + qh) * D : nullptr, c);
+    T::load_q(Q, col_ok ? reinterpret_cast<const QT*>(a.q) + row * D : nullptr, c);
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;  // raw score -> base-2 logit (C > 0)
 
@@ -105,7 +120,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
         const f32x4 sc = T::qk(R, Q);
         float t[4] = {sc[0], sc[1], sc[2], sc[3]};
         const int valid = L - jj * kBS;
-        if (valid < kBS) {  // tail block: mask tokens past L (scores and V)
+        if constexpr (MQ) {
+            // causal: column r sees tokens below lim; V rows past L are masked
+            if (lim_min - jj * kBS < kBS) {
+                const int vcol = lim - jj * kBS;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * c + e >= vcol) t[e] = -INFINITY;
+                if (valid < kBS) T::mask_v(R, c, valid);
+            }
+        } else if (valid < kBS) {  // tail block: mask tokens past L (scores and V)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (4 * c + e >= valid) t[e] = -INFINITY;
@@ -115,15 +139,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
         bm = group_max4(bm);
         const float mn = fmaxf(m, bm);
         if (__ballot((mn - m) * C > kRescaleLog2)) {  // some column's max jumped: rescale
-            const float alpha = fast_exp2((m - mn) * C);
+            // (MQ) a column with no key yet keeps alpha = 1 (its m and mn are -inf)
+            const float alpha = (MQ && mn == -INFINITY) ? 1.f : fast_exp2((m - mn) * C);
             l *= alpha;
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[n] *= alpha;
             m = mn;
         }
+        // with MQ a column may have seen no key yet (m = -inf, all its
+        // scores -inf): its weights must be 0, not exp2(NaN)
+        const float mref = (MQ && m == -INFINITY) ? 0.f : m;
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - m) * C);
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2((t[e] - mref) * C);
         l += (p[0] + p[1]) + (p[2] + p[3]);  // this lane's tokens; reduced after the loop
         T::pv(R, p, acc);
     };
@@ -185,13 +213,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
             float M = m;
 #pragma unroll
             for (int v = 0; v < WAVES - 1; ++v) M = fmaxf(M, s_m[v * 16 + r]);
-            const float f0 = fast_exp2((m - M) * C);  // wave 0 always has a block: M finite
+            // M is finite unless (MQ) the column saw no key in any wave
+            const float f0 = (MQ && M == -INFINITY) ? 0.f : fast_exp2((m - M) * C);
             l *= f0;
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[n] *= f0;
 #pragma unroll
             for (int v = 0; v < WAVES - 1; ++v) {
-                const float f = fast_exp2((s_m[v * 16 + r] - M) * C);  // 0 for a wave without blocks
+                // 0 for a wave without blocks (or, with MQ, without keys of this column)
+                const float f = (MQ && M == -INFINITY) ? 0.f : fast_exp2((s_m[v * 16 + r] - M) * C);
                 l += f * s_l[v * 16 + r];
 #pragma unroll
                 for (int n = 0; n < NT; ++n)
@@ -204,19 +234,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
 
     if (w > 0 || !col_ok) return;
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
-    const float inv = vscale / l;
+    // l = 0 only for a column that saw no key (MQ): zeros, lse -inf
+    const float inv = (MQ && !(l > 0.f)) ? 0.f : vscale / l;
     // the one-pass mode, and a split sequence with a single partition when
     // asked to, write the output here
     const int np = (nblk + pb - 1) / pb;
     if (!SPLIT || (np == 1 && a.single_direct)) {
-        QT* o = reinterpret_cast<QT*>(a.out) + ((size_t)b * Hq + qh) * D;
+        QT* o = reinterpret_cast<QT*>(a.out) + row * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
             store4(o + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv,
                    acc[n][3] * inv);
         return;
     }
-    const size_t row = (size_t)b * Hq + qh;
     float* po = a.part_out + (row * a.max_parts + part) * D;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -230,17 +260,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;
 
-template <int D, int KIND, bool SPLIT>
+template <int D, int KIND, bool SPLIT, bool MQ>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), SPLIT ? (unsigned)a.grid_parts : 1u);
-    hipLaunchKernelGGL((decode_kernel<D, KIND, SPLIT, kWaves>), grid,
+    hipLaunchKernelGGL((decode_kernel<D, KIND, SPLIT, MQ, kWaves>), grid,
                        dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 
+template <int D, int KIND, bool MQ>
+hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
+    return a.partition_blocks > 0 ? launch_t<D, KIND, true, MQ>(a, s)
+                                  : launch_t<D, KIND, false, MQ>(a, s);
+}
+
 template <int D, int KIND>
 hipError_t launch_kind(const DecodeArgs& a, hipStream_t s) {
-    return a.partition_blocks > 0 ? launch_t<D, KIND, true>(a, s) : launch_t<D, KIND, false>(a, s);
+    return a.q_len > 1 ? launch_mq<D, KIND, true>(a, s) : launch_mq<D, KIND, false>(a, s);
 }
 
 template <int D>

@@ -25,6 +25,7 @@ struct DecodeArgs {
     int q_dtype;          // pa_dtype
     int kv_dtype;         // pa_dtype
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int q_len;            // queries per sequence (the newest q_len cached tokens), q_len * G <= 16
     int max_blocks_per_seq;
     int partition_blocks; // blocks per partition; 0 = whole sequence in one pass
     int grid_parts;       // partitions in the grid (1 in one-pass mode)
@@ -57,6 +58,7 @@ struct PrefillArgs {
     const float* v_scale;
     int q_dtype, kv_dtype;
     int num_chunks, num_q_heads, num_kv_heads, head_dim;
+    int uniform_q_len;    // > 0: chunk c owns rows c*uniform_q_len .. (cu_q_lens unused)
     int max_blocks_per_seq;
     float scale;
 };

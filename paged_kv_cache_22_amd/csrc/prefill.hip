@@ -50,13 +50,29 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
     const int ch = blockIdx.x / Hkv;
-    const int qbeg = a.cu_q_lens[ch];
-    const int qlen = a.cu_q_lens[ch + 1] - qbeg;
+    const int qbeg = a.uniform_q_len > 0 ? ch * a.uniform_q_len : a.cu_q_lens[ch];
+    const int qlen = a.uniform_q_len > 0 ? a.uniform_q_len : a.cu_q_lens[ch + 1] - qbeg;
     const int L = a.seq_lens[ch];
     const int ctx = L - qlen;
     const int nrho = qlen * G;
     const int rho_wg = blockIdx.y * (16 * NC * kWaves);
-    if (rho_wg >= nrho || ctx < 0) return;  // uniform; ctx < 0 breaks the contract: read nothing
+    if (rho_wg >= nrho) return;  // uniform
+    if (ctx < 0) {
+        // fewer cached tokens than queries (an idle sequence has none): the
+        // rows see no keys; they get zeros and lse -inf, and nothing is read
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            const int rho = rho_wg + w * 16 * NC + 16 * ct + r;
+            if (rho >= nrho) continue;
+            const int i = rho / G, g = rho - (rho / G) * G;
+            const size_t qrow = (size_t)(qbeg + i) * Hq + h * G + g;
+            QT* o = reinterpret_cast<QT*>(a.out) + qrow * D;
+#pragma unroll
+            for (int n = 0; n < T::NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
+            if (a.out_lse && c == 0) a.out_lse[qrow] = -INFINITY;
+        }
+        return;
+    }
 
     // key blocks the workgroup needs, and this wave's share of the rows
     const int nblk = (ctx + (min(nrho, rho_wg + 16 * NC * kWaves) - 1) / G) / kBS + 1;

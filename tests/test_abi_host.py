@@ -203,3 +203,23 @@ def test_empty_calls_accept_null_arrays():
              0, 0.08, None, None, None) == OK
     assert p(None, None, None, 1, P, 0, 0, P, P, 1, P, 160, P, 4, 32, 8, 128, 16,
              9000, 0.08, None, None, None) == OK                  # chunks all empty
+
+
+def test_multi_query_rejects():
+    f = pa.lib.pa_decode_multi_query
+
+    def call(**over):
+        a = dict(out=P, q=P, qd=1, qn=4, k=P, v=P, kvd=1, bt=P, mb=256, sl=P, B=64, hq=32, hkv=8,
+                 d=128, bs=16, nb=9000, scale=0.088, ks=None, vs=None, part=512, max_len=4096,
+                 ws=P, wsb=1 << 30, stream=None)
+        a.update(over)
+        return f(*a.values())
+
+    assert call(qn=0) == SHAPE
+    assert call(qn=-2) == SHAPE
+    assert call(out=None) == NULL
+    assert call(d=96) == UNSUP
+    assert call(ws=None) == WS                    # 4 x 32 rows per sequence need partials
+    assert call(B=0, out=None, q=None, ws=None) == OK
+    need = pa.decode_workspace_size(64, 4 * 32, 128, 4096, 512)
+    assert call(wsb=need - 1) == WS

@@ -108,9 +108,10 @@ def kv_bytes_per_token(num_kv_heads: int, head_dim: int, kv_bytes: float,
 # ---------------------------------------------------------------------------
 @dataclasses.dataclass
 class DecodeWorkload:
-    """One decode query per sequence over a paged KV cache."""
+    """Decode queries over a paged KV cache: one per sequence, or (q_len > 1)
+    the newest q_len cached tokens of each sequence."""
     name: str
-    q: np.ndarray                 # [B, Hq, d]   f32 / bf16 bits
+    q: np.ndarray                 # [B, Hq, d], or [B, q_len, Hq, d]; f32 / bf16 bits
     k_cache: np.ndarray           # [NB, Hkv, d/X, bs, X]
     v_cache: np.ndarray           # [NB, Hkv, d, bs]
     block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
@@ -125,9 +126,11 @@ class DecodeWorkload:
     @property
     def num_seqs(self) -> int: return int(self.q.shape[0])
     @property
-    def num_q_heads(self) -> int: return int(self.q.shape[1])
+    def q_len(self) -> int: return int(self.q.shape[1]) if self.q.ndim == 4 else 1
     @property
-    def head_dim(self) -> int: return int(self.q.shape[2])
+    def num_q_heads(self) -> int: return int(self.q.shape[-2])
+    @property
+    def head_dim(self) -> int: return int(self.q.shape[-1])
     @property
     def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
     @property
@@ -285,9 +288,11 @@ def _draw_q(rng, shape, q_dtype):
 def decode_workload(*, seed: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
                     head_dim: int, len_lo: int, len_hi: int, q_dtype: str, kv_dtype: str,
                     block_size: int = BLOCK_SIZE, pool_blocks: Optional[int] = None,
-                    partition_size: int = 0, pad: int = -1, seq_lens=None,
+                    partition_size: int = 0, pad: int = -1, seq_lens=None, q_len: int = 0,
                     name: str = "decode") -> DecodeWorkload:
-    """Generic seeded decode workload (lengths uniform integers in [lo, hi])."""
+    """Generic seeded decode workload (lengths uniform integers in [lo, hi]).
+    ``q_len`` > 0 gives q the shape [B, q_len, Hq, d] (several queries per
+    sequence); 0 keeps the plain [B, Hq, d]."""
     rng = np.random.default_rng(seed)
     if seq_lens is None:
         lens = rng.integers(len_lo, len_hi, size=num_seqs, endpoint=True).astype(np.int32)
@@ -300,7 +305,9 @@ def decode_workload(*, seed: int, num_seqs: int, num_q_heads: int, num_kv_heads:
     perm = rng.permutation(nb).astype(np.int32)
     max_blocks = max(1, -(-int(lens.max(initial=0)) // block_size))
     table, _ = _tables_from_perm(perm, lens, block_size, max_blocks, pad)
-    q = _draw_q(rng, (num_seqs, num_q_heads, head_dim), q_dtype)
+    qshape = (num_seqs, num_q_heads, head_dim) if q_len == 0 else \
+        (num_seqs, q_len, num_q_heads, head_dim)
+    q = _draw_q(rng, qshape, q_dtype)
     k, v, ks, vs = _make_pools(seed, nb, num_kv_heads, head_dim, block_size, kv_dtype)
     return DecodeWorkload(name=name, q=q, k_cache=k, v_cache=v, block_table=table,
                           seq_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype,
