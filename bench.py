@@ -14,8 +14,9 @@ lines behind, so no write-back of the flush lands inside the next timed
 kernel.  Step times come from HIP events on the launch stream.
 
 The other workloads (long-context split-KV, the mixed chunked-prefill step,
-fp8 KV, and the cache writes that precede attention) are timed the same way
-and reported under "per_config".  The
+fp8 KV, the cache writes that precede attention, and draft verification with
+several queries per sequence) are timed the same way and reported under
+"per_config".  The
 CPU-baseline leg times the fp64 oracle on the host over the whole headline
 batch (single thread).
 
@@ -183,6 +184,57 @@ def time_prefill(torch, pa, d, wl, steps, warmup, flush):
     return [t.ms(i, 0, 1) for i in range(steps)]
 
 
+def time_verify(torch, pa, W, steps, warmup, flush, partition_size):
+    """Draft verification at the Llama-3-8B layer shape: 64 sequences of
+    512-4096 tokens, 4 queries each (pa_decode_multi_query, the 16 MFMA
+    columns filled by 4 queries x 4 heads), against the same work done as 64
+    prefill chunks of 4 rows (pa_prefill_chunk)."""
+    from workloads.device import Dev
+    wl = W.decode_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=512, len_hi=4096, q_dtype="bf16", kv_dtype="bf16", q_len=4,
+                           pad=0, name="verify")
+    d = Dev(wl)
+    B, qn = wl.num_seqs, wl.q_len
+    out = torch.empty_like(d.q)
+    ws = torch.empty(max(pa.decode_workspace_size(B, qn * wl.num_q_heads, wl.head_dim,
+                                                  wl.max_seq_len, partition_size), 256),
+                     dtype=torch.uint8, device="cuda")
+    q3 = d.q.reshape(B * qn, wl.num_q_heads, wl.head_dim)
+    out3 = torch.empty_like(q3)
+    cu = torch.arange(0, B * qn + 1, qn, dtype=torch.int32, device="cuda")
+
+    def mq(ev):
+        ev[0].record()
+        pa.decode_multi_query(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                              scale=wl.scale, partition_size=partition_size, out=out, workspace=ws)
+        ev[1].record()
+
+    def pf(ev):
+        ev[0].record()
+        pa.prefill_chunk(q3, cu, d.k, d.v, d.bt, d.sl, max_q_len=qn, scale=wl.scale, out=out3)
+        ev[1].record()
+
+    res = {"workload": "draft verification: 64 seqs x 4 queries, lens U[512,4096] seed 2, "
+                       "32/8 heads, d=128, bf16", "partition_size": partition_size}
+    for name, fn in (("multi_query_decode", mq), ("as_prefill_chunks", pf)):
+        wt = Timer(torch, warmup, 2)
+        for i in range(warmup):
+            flush()
+            fn(wt.ev[i])
+        torch.cuda.synchronize()
+        t = Timer(torch, steps, 2)
+        for i in range(steps):
+            flush()
+            fn(t.ev[i])
+        torch.cuda.synchronize()
+        ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
+        res[name] = {"ms": round(ms, 5), "kv_GBps": round(wl.kv_bytes() / ms / 1e6, 2),
+                     "pct_hbm_peak": round(100 * wl.kv_bytes() / ms / 1e6 / HBM_PEAK_GBS, 2),
+                     "queries_per_s": round(B * qn / ms * 1e3, 1)}
+    res["kv_bytes"] = wl.kv_bytes()
+    return res
+
+
 def write_cases(W):
     """Cache writes of the decode and prefill steps above, and a long-context
     fill: (label, WriteWorkload, pool blocks).  The caches are allocated on
@@ -282,6 +334,10 @@ def profile_one(args, W):
     import paged_kv_cache_22_amd as pa
     from workloads.device import Dev
     flush = CacheFlush(torch)
+    if args.workload == "VERIFY":
+        print(json.dumps(time_verify(torch, pa, W, args.steps, args.warmup, flush,
+                                     args.partition_size)), flush=True)
+        return
     if args.workload == "WRITE":
         for wl in write_cases(W):
             print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
@@ -314,9 +370,10 @@ def main():
     ap.add_argument("--partition-size", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE"],
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY"],
                     help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
-                         "plus the others under per_config; WRITE = the cache writes)")
+                         "plus the others under per_config; WRITE = the cache writes, VERIFY = draft "
+                         "verification)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -383,6 +440,7 @@ def main():
         }
         del dd, dp
         per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
+        per_config["verify"] = time_verify(torch, pa, W, 20, 3, flush, args.partition_size)
 
     kv = head["kv_GBps"]
     line = {
