@@ -1,0 +1,58 @@
+"""Device code built with the library's own flags (CPU only, hipcc cross-compiles
+for gfx950): no packed-fp32 VALU forms anywhere, and every kernel within the
+register budget without scratch spills."""
+import glob
+import importlib.util
+import os
+import re
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "paged_kv_cache_22_amd", "csrc")
+
+
+def _build_module():
+    spec = importlib.util.spec_from_file_location(
+        "_pa_build_isa", os.path.join(ROOT, "paged_kv_cache_22_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    B = _build_module()
+    try:
+        hipcc = B._hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa")
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def one(src):
+        dst = os.path.join(out, os.path.basename(src) + ".s")
+        p = subprocess.run([hipcc, *B.HIP_FLAGS, "--cuda-device-only", "-S", src, "-o", dst],
+                           capture_output=True, text=True)
+        assert p.returncode == 0, p.stderr[-2000:]
+        return os.path.basename(src), open(dst).read()
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        return dict(ex.map(one, srcs))
+
+
+def test_no_packed_fp32_valu(device_asm):
+    pat = re.compile(r"^\s*v_pk_(add|mul|fma)_f32\b", re.M)
+    for name, text in device_asm.items():
+        hits = pat.findall(text)
+        assert not hits, f"{name}: {len(hits)} packed-fp32 instructions"
+
+
+def test_no_scratch_spills(device_asm):
+    for name, text in device_asm.items():
+        sizes = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
+        assert sizes, f"{name}: no kernel descriptors found"
+        assert all(int(x) == 0 for x in sizes), f"{name}: a kernel uses scratch ({sizes})"
