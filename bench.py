@@ -5,8 +5,9 @@ Headline: KV GB/s (and % of the 8 TB/s HBM peak) plus tokens-attended/s of
 bf16 decode at the Llama-3-8B layer shape: 64 sequences, 32 q-heads / 8
 kv-heads, head_dim 128, block_size 16, lengths uniform in [512, 4096] (seed
 2), block tables a random permutation of one pool.  A step is one pass of
-the decode path over that batch: pa_decode (the split-KV partition kernel,
-then the log-sum-exp merge for sequences with several partitions), inputs
+the decode path over that batch: pa_decode in its balanced split-KV mode
+(the attention kernel over equal block ranges, one per resident workgroup,
+then the log-sum-exp merge for sequences split over several ranges), inputs
 resident in HBM.  Before
 every timed step a 1 GiB buffer is read (a reduction into one scalar) so no
 input survives in the L2 or the 256 MB Infinity Cache; a read leaves clean
@@ -136,18 +137,18 @@ def time_decode(torch, pa, d, wl, P, steps, warmup, flush):
 
 
 def time_partition_kernel(torch, pa, d, wl, P, steps, warmup, flush):
-    """Per-launch ms of the split-KV partition kernel alone (pa_decode_partitions),
-    HIP events on the launch stream."""
-    pmax = -(-wl.max_seq_len // P)
-    po = torch.empty((wl.num_seqs, wl.num_q_heads, pmax, wl.head_dim), dtype=torch.float32,
-                     device="cuda")
-    pl = torch.empty((wl.num_seqs, wl.num_q_heads, pmax), dtype=torch.float32, device="cuda")
+    """Per-launch ms of the attention kernel alone (the attention stage of
+    pa_decode_stages, without the merge), HIP events on the launch stream."""
+    out = torch.empty_like(d.q)
+    ws = torch.empty(max(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                                  wl.max_seq_len, P), 256),
+                     dtype=torch.uint8, device="cuda")
 
     def launch(ev):
         ev[0].record()
-        pa.decode_partitions(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
-                             partition_size=P, scale=wl.scale, k_scale=d.ks, v_scale=d.vs,
-                             partial_out=po, partial_lse=pl)
+        pa.decode_stages(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                         stages=pa.PA_STAGE_ATTENTION, out=out, workspace=ws,
+                         partition_size=P, scale=wl.scale, k_scale=d.ks, v_scale=d.vs)
         ev[1].record()
 
     for i in range(warmup):
@@ -338,6 +339,8 @@ def profile_one(args, W):
         print(json.dumps(time_verify(torch, pa, W, args.steps, args.warmup, flush,
                                      args.partition_size)), flush=True)
         return
+    if args.partition_size < 0 and args.workload in ("C4", "C5"):
+        args.partition_size = 1024   # the per-config default of these workloads
     if args.workload == "WRITE":
         for wl in write_cases(W):
             print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
@@ -345,7 +348,7 @@ def profile_one(args, W):
     n = int(args.workload[1])
     res = {"workload": W.CONFIG_NAMES[n]}
     if n == 4:
-        m = W.config4(pad=0, partition_size=args.partition_size)
+        m = W.config4(pad=0, partition_size=1024)
         dd, dp = Dev(m.decode), Dev(m.prefill)
         s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, args.steps,
                            args.warmup, flush)
@@ -367,7 +370,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-size", type=int, default=1024)
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="split-KV partition size in tokens for the headline; -1 = the "
+                         "balanced split (equal work per resident workgroup), 0 = one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY"],
@@ -405,7 +410,7 @@ def main():
     step_ms, _ = time_decode(torch, pa, d, wl, args.partition_size, args.steps,
                              args.warmup, flush)
     wall = time.perf_counter() - t0
-    if args.partition_size > 0:   # the dominant kernel on its own
+    if args.partition_size != 0:   # the dominant kernel on its own
         kern_ms = time_partition_kernel(torch, pa, d, wl, args.partition_size, args.steps,
                                         args.warmup, flush)
     else:
@@ -415,14 +420,20 @@ def main():
 
     per_config = {}
     if not args.headline_only:
-        for n, P in ((3, 512), (5, args.partition_size)):
+        # C3 at its stated 512-token partitions, C5 at fixed 1024-token
+        # partitions (its best: short, similar lengths), each also balanced
+        for n, P in ((3, 512), (5, 1024)):
             w = W.build_config(n, pad=0) if n == 3 else W.build_config(n, pad=0, partition_size=P)
             dd = Dev(w)
-            s, k = time_decode(torch, pa, dd, w, w.partition_size, 20, 3, flush)
+            s, k = time_decode(torch, pa, dd, w, P, 20, 3, flush)
             per_config[w.name] = decode_summary(w, s, k)
             per_config[w.name]["workload"] = W.CONFIG_NAMES[n]
+            per_config[w.name]["partition_size"] = P
+            s, k = time_decode(torch, pa, dd, w, -1, 20, 3, flush)
+            per_config[w.name]["balanced"] = {kk: vv for kk, vv in decode_summary(w, s, k).items()
+                                              if kk in ("ms_per_step", "kv_GBps", "pct_hbm_peak")}
             del dd
-        m = W.config4(pad=0, partition_size=args.partition_size)
+        m = W.config4(pad=0, partition_size=1024)
         dd, dp = Dev(m.decode), Dev(m.prefill)
         s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, 20, 3, flush)
         pms = time_prefill(torch, pa, dp, m.prefill, 20, 3, flush)
@@ -469,7 +480,8 @@ def main():
                    "note": "per-step HIP events around the launches; a 1 GiB rewrite before "
                            "each step evicts the Infinity Cache and is not timed"},
         "roofline": {
-            "kernel": "decode_kernel<128, bf16, split> (pa_decode_partitions)",
+            "kernel": ("decode_balanced_kernel<128, bf16>" if args.partition_size < 0 else
+                       "decode_kernel<128, bf16, split>") + " (attention stage of pa_decode_stages)",
             "bound": "hbm",
             "achieved": head["partition_kernel_GBps"],
             "peak": HBM_PEAK_GBS,
@@ -478,10 +490,11 @@ def main():
             "traffic": stored_traffic(args.partition_size),
             "algorithmic_bytes_per_launch": head["kv_bytes"],
             "avg_launch_ms": head["partition_kernel_ms"],
-            "note": "achieved = live K+V bytes / mean HIP-event duration of the partition "
-                    "kernel launched alone; traffic = HBM bytes read+written per launch from "
-                    "the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), "
-                    "null if the kernel sources changed since",
+            "note": "achieved = live K+V bytes / mean HIP-event duration of the attention "
+                    "kernel launched alone (without the merge); traffic = HBM bytes "
+                    "read+written per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                    "summary (copy-calibrated), null if the kernel sources or the partition "
+                    "mode changed since",
         },
         "cpu_baseline": cpu,
         "per_config": per_config,

@@ -81,6 +81,15 @@ typedef enum {
     PA_ERR_HIP = 7           /* the HIP runtime rejected a launch */
 } pa_status;
 
+/* partition_size value selecting the balanced split-KV mode of pa_decode and
+ * pa_decode_multi_query (see pa_decode). */
+#define PA_PARTITION_BALANCED (-1)
+
+/* Stages of pa_decode_stages. */
+#define PA_STAGE_ATTENTION 1  /* the attention kernel (partials, or direct rows) */
+#define PA_STAGE_MERGE 2      /* the log-sum-exp merge of the partials */
+#define PA_STAGE_ALL 3
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* pa_status_string(int status);
 
@@ -88,10 +97,13 @@ const char* pa_status_string(int status);
 int pa_version(void);
 
 /*
- * Bytes of workspace pa_decode needs: 0 when partition_size == 0, else room
- * for fp32 partials [num_seqs, num_q_heads, P_max, head_dim] and their lse
- * [num_seqs, num_q_heads, P_max], P_max = ceil(max_seq_len / partition_size),
- * each region 256-byte aligned.  Returns 0 for invalid arguments.
+ * Bytes of workspace pa_decode needs: 0 when partition_size == 0; for
+ * partition_size > 0 room for fp32 partials [num_seqs, num_q_heads, P_max,
+ * head_dim] and their lse [num_seqs, num_q_heads, P_max], P_max =
+ * ceil(max_seq_len / partition_size); for PA_PARTITION_BALANCED room for
+ * num_seqs piece records (2 int32) and the partials of up to
+ * 1024 + num_seqs pieces of num_q_heads rows each.  Each region is 256-byte
+ * aligned.  Returns 0 for invalid arguments.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                 int max_seq_len, int partition_size);
@@ -107,6 +119,15 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * pa_merge_partitions) writes out.  A sequence that fits in one partition
  * is written directly by the partition kernel (bit-identical to merging its
  * single partition).  A workspace serves one call at a time.
+ *
+ * partition_size == PA_PARTITION_BALANCED: the blocks of all sequences, laid
+ * end to end per kv-head, are cut into equal ranges, one per workgroup, with
+ * as many workgroups as the device holds at once (measured once per device
+ * with the runtime's occupancy query); a range covering parts of
+ * several sequences yields one partial per part, and the merge combines each
+ * sequence's parts.  Every workgroup then streams the same number of bytes
+ * whatever the mix of lengths.  Results equal the other modes up to the
+ * rounding of the merge.
  * max_seq_len is the caller's host-side
  * bound on seq_lens; it sizes the grid.  A sequence of length 0 gets zeros.
  * scale is the softmax scale (1/sqrt(head_dim) for plain attention); it
@@ -148,6 +169,24 @@ int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len,
                           int num_blocks, float scale, const float* k_scale,
                           const float* v_scale, int partition_size, int max_seq_len,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_multi_query (q_len = 1: pa_decode) split into its two stages:
+ * `stages` is a mask of PA_STAGE_ATTENTION and PA_STAGE_MERGE.  Running the
+ * attention stage, then (on the same stream, with the same arguments and
+ * workspace) the merge stage equals one PA_STAGE_ALL call; other work, or
+ * timing events, may go between the two.  Only the decode kernel's packings
+ * (q_len * G <= 16) are accepted.  One-pass calls (partition_size 0) have no
+ * merge: their merge stage does nothing.
+ */
+int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len,
+                     const void* k_cache, const void* v_cache, int kv_dtype,
+                     const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, float scale, const float* k_scale,
+                     const float* v_scale, int partition_size, int max_seq_len,
+                     void* workspace, size_t workspace_bytes, int stages, void* stream);
 
 /*
  * Split-KV decode, partition kernel only: writes partial_out / partial_lse

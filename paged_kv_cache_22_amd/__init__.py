@@ -11,11 +11,13 @@ ABI of ``include/pa.h``); this package is its thin Python binding:
 Importing the package loads ``libpa.so`` and fails if it is not built
 (``python paged_kv_cache_22_amd/build.py``).
 """
-from ._binding import (LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, PAError, decode,
-                       decode_multi_query,
+from ._binding import (LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALANCED, PAError, decode,
+                       decode_multi_query, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
+                       PA_STAGE_ALL,
                        decode_partitions, decode_workspace_size, lib, merge_partitions,
                        prefill_chunk, status_string, write_kv)
 
-__all__ = ["decode", "decode_multi_query", "decode_partitions", "merge_partitions", "prefill_chunk", "write_kv",
+__all__ = ["decode", "decode_multi_query", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
+           "PA_STAGE_ALL", "decode_partitions", "merge_partitions", "prefill_chunk", "write_kv",
            "decode_workspace_size", "status_string", "PAError", "lib", "LIB_PATH",
-           "PA_F32", "PA_BF16", "PA_FP8_E4M3"]
+           "PA_F32", "PA_BF16", "PA_FP8_E4M3", "PA_PARTITION_BALANCED"]

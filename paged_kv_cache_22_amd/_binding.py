@@ -13,6 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_PARTITION_BALANCED = -1   # partition_size selecting the balanced split-KV mode
+PA_STAGE_ATTENTION, PA_STAGE_MERGE, PA_STAGE_ALL = 1, 2, 3
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
                 4: "PA_ERR_ALIGN", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP"}
 
@@ -27,6 +29,8 @@ SIGNATURES = {
                        _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "pa_decode_multi_query": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
                                    _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "pa_decode_stages": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
+                              _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _i, _vp]),
     "pa_decode_partitions": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i,
                                   _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "pa_merge_partitions": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -177,6 +181,28 @@ def decode_multi_query(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_le
                                    _dev(v_scale, "v_scale"), int(partition_size), int(max_seq_len),
                                    _dev(workspace, "workspace"), ws_bytes, _stream(q))
     _check("pa_decode_multi_query", st)
+    return out
+
+
+def decode_stages(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int, stages: int,
+                  out, workspace, scale: Optional[float] = None, partition_size: int = 0,
+                  k_scale=None, v_scale=None):
+    """pa_decode_stages: run the attention and/or merge stage of a decode
+    (q [B, Hq, d] or [B, q_len, Hq, d]) on caller-owned out and workspace."""
+    qn = q.shape[1] if q.dim() == 4 else 1
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+    _, _, _, NB, Hkv, bs = _kv_dims(q.reshape(B, qn * Hq, d), k_cache, v_cache)
+    if scale is None:
+        scale = d ** -0.5
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_stages(_dev(out, "out"), _dev(q, "q"), _dtype_code(q, False), qn,
+                              _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dtype_code(k_cache, True), _dev(block_table, "block_table"),
+                              block_table.shape[1], _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d, bs,
+                              NB, float(scale), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                              int(partition_size), int(max_seq_len), _dev(workspace, "workspace"),
+                              ws_bytes, int(stages), _stream(q))
+    _check("pa_decode_stages", st)
     return out
 
 

@@ -16,6 +16,7 @@ constexpr int kMaxGroup = 16;          // q-heads per kv-head handled by one wav
 constexpr int kMaxGridY = 65535;
 constexpr size_t kRegionAlign = 256;
 
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -64,8 +65,8 @@ int decode_checks(const void* q, int q_dtype, const void* k_cache, const void* v
     if (num_seqs < 0 || max_seq_len < 0) return PA_ERR_SHAPE;
     if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
     if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-    if (partition_size < 0) return PA_ERR_SHAPE;
-    if (partition_size % block_size != 0) return PA_ERR_UNSUPPORTED;
+    if (partition_size < 0 && partition_size != PA_PARTITION_BALANCED) return PA_ERR_SHAPE;
+    if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_UNSUPPORTED;
     if (partition_size > 0) {
         const long long parts = ((long long)max_seq_len + partition_size - 1) / partition_size;
         if (parts > kMaxGridY) return PA_ERR_UNSUPPORTED;
@@ -123,9 +124,16 @@ int pa_version(void) { return 100; }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
                                 int partition_size) {
-    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size < 0)
-        return 0;
-    if (partition_size == 0) return 0;
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return 0;
+    if (partition_size == PA_PARTITION_BALANCED) {
+        // piece records | partial outputs | partial lse, for up to
+        // kMaxBalancedSplits splits per kv-head
+        const size_t slots = (size_t)pa::kMaxBalancedSplits + num_seqs;
+        return round_up((size_t)num_seqs * 2 * sizeof(int32_t), kRegionAlign) +
+               round_up(slots * num_q_heads * head_dim * sizeof(float), kRegionAlign) +
+               round_up(slots * num_q_heads * sizeof(float), kRegionAlign);
+    }
+    if (partition_size <= 0) return 0;
     const size_t parts = ((size_t)max_seq_len + partition_size - 1) / partition_size;
     const size_t rows = (size_t)num_seqs * num_q_heads * parts;
     return round_up(rows * head_dim * sizeof(float), kRegionAlign) +
@@ -142,7 +150,7 @@ int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partiti
                            seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
     if (st != PA_OK) return st;
-    if (partition_size == 0) return PA_ERR_UNSUPPORTED;
+    if (partition_size <= 0) return PA_ERR_UNSUPPORTED;
     if (num_seqs > 0 && (!partial_out || !partial_lse)) return PA_ERR_NULL;
     if (!aligned16(partial_out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u)) return PA_ERR_ALIGN;
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
@@ -198,7 +206,8 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
                 int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, float scale, const float* k_scale,
                 const float* v_scale, int partition_size, int max_seq_len, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, int stages = PA_STAGE_ALL) {
+    const bool run_attn = stages & PA_STAGE_ATTENTION, run_merge = stages & PA_STAGE_MERGE;
     const int rows_per_seq = q_len * num_q_heads;   // output rows of one sequence
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
                                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
@@ -209,19 +218,52 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
         a.out = out;
         a.partition_blocks = 0;
         a.grid_parts = 1;
-        return hip_status(pa::launch_decode(a, stream));
+        return run_attn ? hip_status(pa::launch_decode(a, stream)) : PA_OK;
     }
     const size_t need = pa_decode_workspace_size(num_seqs, rows_per_seq, head_dim, max_seq_len,
                                                  partition_size);
     if (num_seqs > 0 && need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
     if (num_seqs == 0) return PA_OK;
+    if (partition_size == PA_PARTITION_BALANCED) {
+        // workspace: piece records | partial outputs | partial lse
+        const int splits = pa::balanced_splits(a);
+        if (splits < 1) return PA_ERR_HIP;
+        const size_t slots = (size_t)splits + num_seqs;
+        char* ws = reinterpret_cast<char*>(workspace);
+        const size_t off_out = round_up((size_t)num_seqs * 2 * sizeof(int32_t), kRegionAlign);
+        const size_t off_lse = off_out + round_up(slots * rows_per_seq * head_dim * sizeof(float), kRegionAlign);
+        a.out = out;
+        a.piece_info = ws;
+        a.part_out = reinterpret_cast<float*>(ws + off_out);
+        a.part_lse = reinterpret_cast<float*>(ws + off_lse);
+        a.balanced = 1;
+        a.grid_parts = splits;
+        int st = run_attn ? hip_status(pa::launch_decode(a, stream)) : PA_OK;
+        if (st != PA_OK || !run_merge) return st;
+        pa::MergeArgs m{};
+        m.out = out;
+        m.out_dtype = q_dtype;
+        m.part_out = a.part_out;
+        m.part_lse = a.part_lse;
+        m.seq_lens = seq_lens;
+        m.partition_size = 1;
+        m.num_seqs = num_seqs;
+        m.num_q_heads = rows_per_seq;
+        m.head_dim = head_dim;
+        m.skip_single = 1;
+        m.piece_info = ws;
+        m.piece_slots = (int)slots;
+        m.q_len = q_len;
+        m.num_kv_heads = num_kv_heads;
+        return hip_status(pa::launch_merge(m, stream));
+    }
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
     if (parts == 0) {  // every sequence is empty: the one-pass kernel writes the zeros
         a.out = out;
         a.partition_blocks = 0;
         a.grid_parts = 1;
-        return hip_status(pa::launch_decode(a, stream));
+        return run_attn ? hip_status(pa::launch_decode(a, stream)) : PA_OK;
     }
     // workspace: partial outputs | partial lse
     const size_t rows = (size_t)num_seqs * rows_per_seq * parts;
@@ -234,8 +276,8 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
     a.max_parts = parts;
     a.partition_blocks = partition_size / kBlockSize;
     a.grid_parts = parts;
-    int st = hip_status(pa::launch_decode(a, stream));
-    if (st != PA_OK) return st;
+    int st = run_attn ? hip_status(pa::launch_decode(a, stream)) : PA_OK;
+    if (st != PA_OK || !run_merge) return st;
     pa::MergeArgs m{};
     m.out = out;
     m.out_dtype = q_dtype;
@@ -322,6 +364,29 @@ int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len, cons
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale = scale;
     return hip_status(pa::launch_prefill(a, stream));
+}
+
+int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
+                     const void* v_cache, int kv_dtype, const int32_t* block_table,
+                     int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                     const float* k_scale, const float* v_scale, int partition_size,
+                     int max_seq_len, void* workspace, size_t workspace_bytes, int stages,
+                     void* stream) {
+    if (q_len <= 0) return PA_ERR_SHAPE;
+    if (stages < 1 || stages > PA_STAGE_ALL) return PA_ERR_SHAPE;
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    if ((long long)num_seqs * q_len * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if ((long long)q_len * (num_q_heads / num_kv_heads) > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    return decode_impl(out, q, q_dtype, q_len, k_cache, v_cache, kv_dtype, block_table,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
+                       workspace_bytes, stream, stages);
 }
 
 int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, const int32_t* cu_q_lens,

@@ -43,23 +43,36 @@
 namespace pa {
 namespace {
 
-template <int D, int KIND, bool SPLIT, bool MQ, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) {
+// Where one (sequence, kv-head) range's result goes.  direct: the normalised
+// output row; otherwise a partial (output and lse) at partial index
+// prow_base + row * prow_stride (row = the column's output row) or, with
+// prow_stride == 0, prow_base + r (r = the column).
+struct RangeOut {
+    bool direct;
+    size_t prow_base;
+    size_t prow_stride;
+};
+
+// Attention of sequence b (L cached tokens), kv-head h, over its logical
+// blocks [j0, j1) by the workgroup's WAVES waves (j0 < j1).  Wave w takes
+// blocks j0 + w, j0 + w + WAVES, ...; wave 0 combines and writes.
+template <int D, int KIND, bool MQ, int WAVES>
+__device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, int L, int j0, int j1,
+                                             const RangeOut& dst, float* smem) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, known uniform
+    // The thread index goes through an empty asm so that what is derived
+    // from it (load offsets, column indices) is recomputed for every range
+    // instead of being hoisted out of the balanced kernel's piece loop and
+    // held in registers across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
-    const int h = blockIdx.x % Hkv;
-    const int b = blockIdx.x / Hkv;
-    const int part = blockIdx.y;
-    const int L = a.seq_lens[b];
-    const int nblk = (L + kBS - 1) / kBS;
-    const int pb = SPLIT ? a.partition_blocks : nblk;
-    const int j0 = part * pb;
     // column r: query qi (0 without MQ), q-head qh; its output / q row
     const int qn = MQ ? a.q_len : 1;
     const int qi = MQ ? r / G : 0;
@@ -69,16 +82,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     // keys this column sees: 0 .. lim-1 (L without MQ)
     const int lim = L - qn + 1 + qi;
     const int lim_min = L - qn + 1;  // the smallest limit of the sequence's columns
-
-    if (j0 >= nblk) {  // uniform over the workgroup
-        if (!SPLIT && w == 0 && col_ok) {  // empty sequence: zeros
-            QT* o = reinterpret_cast<QT*>(a.out) + row * D;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
-        }
-        return;
-    }
-    const int j1 = min(nblk, j0 + pb);
     // this wave takes blocks j0 + w, j0 + w + WAVES, ...: n_mine of them
     const int n_mine = max(0, (j1 - j0 - w + WAVES - 1) / WAVES);
 
@@ -192,8 +195,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     l = group_sum4(l);
 
     // ---- combine the waves' softmax states through LDS (wave 0 holds the result)
-    constexpr int kCombineFloats = (WAVES - 1) * (NT * 4 * 64 + 32);
-    __shared__ float smem[kCombineFloats > 1 ? kCombineFloats : 1];
     if constexpr (WAVES > 1) {
         float* s_acc = smem;                                  // [WAVES-1][NT*4][64]
         float* s_m = smem + (WAVES - 1) * NT * 4 * 64;       // [WAVES-1][16]
@@ -236,10 +237,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
     // l = 0 only for a column that saw no key (MQ): zeros, lse -inf
     const float inv = (MQ && !(l > 0.f)) ? 0.f : vscale / l;
-    // the one-pass mode, and a split sequence with a single partition when
-    // asked to, write the output here
-    const int np = (nblk + pb - 1) / pb;
-    if (!SPLIT || (np == 1 && a.single_direct)) {
+    if (dst.direct) {
         QT* o = reinterpret_cast<QT*>(a.out) + row * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
@@ -247,12 +245,160 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
                    acc[n][3] * inv);
         return;
     }
-    float* po = a.part_out + (row * a.max_parts + part) * D;
+    const size_t pidx = dst.prow_base + (dst.prow_stride ? row * dst.prow_stride : (size_t)r);
+    float* po = a.part_out + pidx * D;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
         store4(po + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv,
                acc[n][3] * inv);
-    if (c == 0) a.part_lse[row * a.max_parts + part] = (m * C + fast_log2(l)) * kLn2;
+    if (c == 0) a.part_lse[pidx] = (m * C + fast_log2(l)) * kLn2;
+}
+
+
+// LDS floats of the waves' softmax-state combine
+template <int D, int KIND, int WAVES>
+constexpr int combine_floats() {
+    constexpr int f = (WAVES - 1) * (Tile<KIND, D>::NT * 4 * 64 + 32);
+    return f > 1 ? f : 1;
+}
+
+// zeros for every column row of an empty sequence
+template <int D, int KIND, bool MQ>
+__device__ __forceinline__ void zero_rows(const DecodeArgs& a, int b, int h) {
+    using T = Tile<KIND, D>;
+    using QT = typename QType<KIND>::T;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, c = lane >> 4;
+    const int Hq = a.num_q_heads, G = Hq / a.num_kv_heads;
+    const int qn = MQ ? a.q_len : 1;
+    const int qi = MQ ? r / G : 0;
+    const int qh = h * G + (MQ ? r - qi * G : r);
+    if (r >= qn * G) return;
+    QT* o = reinterpret_cast<QT*>(a.out) + (((size_t)b * qn + qi) * Hq + qh) * D;
+#pragma unroll
+    for (int n = 0; n < T::NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
+}
+
+// One workgroup per (sequence, kv-head, partition): the one-pass mode
+// (SPLIT = false, one partition) and the fixed-size split-KV mode.
+template <int D, int KIND, bool SPLIT, bool MQ, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) {
+    __shared__ float smem[combine_floats<D, KIND, WAVES>()];
+    const int Hkv = a.num_kv_heads;
+    const int h = blockIdx.x % Hkv;
+    const int b = blockIdx.x / Hkv;
+    const int part = blockIdx.y;
+    const int L = a.seq_lens[b];
+    const int nblk = (L + kBS - 1) / kBS;
+    const int pb = SPLIT ? a.partition_blocks : nblk;
+    const int j0 = part * pb;
+    if (j0 >= nblk) {  // uniform over the workgroup
+        if (!SPLIT && (threadIdx.x >> 6) == 0) zero_rows<D, KIND, MQ>(a, b, h);  // empty sequence
+        return;
+    }
+    const int j1 = min(nblk, j0 + pb);
+    // the one-pass mode, and a split sequence with a single partition when
+    // asked to, write the output directly
+    const int np = (nblk + pb - 1) / pb;
+    RangeOut dst;
+    dst.direct = !SPLIT || (np == 1 && a.single_direct);
+    dst.prow_base = (size_t)part;
+    dst.prow_stride = (size_t)a.max_parts;
+    attend_range<D, KIND, MQ, WAVES>(a, b, h, L, j0, j1, dst, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split-KV.  For one kv-head, the sequences' blocks laid end to end
+// form W = sum_b ceil(L_b / 16) units; split s of S owns units
+// [s*W/S, (s+1)*W/S), so every workgroup streams the same number of blocks
+// whatever the length mix, and S * Hkv matches the workgroups the chip holds
+// at once.  A split's range may cover pieces of several sequences; each piece
+// is one attend_range.  A sequence owned by one split only is written
+// directly; otherwise its pieces go to partial slot s + b (strictly
+// increasing along the pieces, so unique, and contiguous for one sequence)
+// and the first piece's workgroup of kv-head 0 records (first slot, count)
+// for the merge.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// the split that owns unit x: the largest s with floor(s * W / S) <= x
+__device__ __forceinline__ int owner(long long x, long long W, int S) {
+    return (int)(((x + 1) * S - 1) / W);
+}
+
+template <int D, int KIND, bool MQ, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const DecodeArgs a) {
+    __shared__ float smem[combine_floats<D, KIND, WAVES>()];
+    const int lane = threadIdx.x & 63;
+    const int s = blockIdx.x;
+    const int h = blockIdx.y;
+    const int B = a.num_seqs;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int cols = (MQ ? a.q_len : 1) * G;   // output rows of one (piece, kv-head)
+
+    // W: every wave sums ceil(L / 16) over the batch, 64 sequences at a time
+    // (all bookkeeping below is wave-uniform: scalar registers)
+    int W = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        W += __builtin_amdgcn_readfirstlane(wave_sum_i(bb < B ? (a.seq_lens[bb] + kBS - 1) / kBS : 0));
+    }
+    // with fewer units than workgroups only the first W split (one unit
+    // each): every split in use then owns at least one unit, so the splits
+    // from a sequence's first to its last all hold a piece of it
+    const int S = min((int)gridDim.x, W);
+    if (s >= S) return;  // uniform
+    const int start = (int)((long long)s * W / S), end = (int)((long long)(s + 1) * W / S);
+
+    // the sequence holding unit `start`, and the units before it
+    int b = 0, cum = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int n = bb < B ? (a.seq_lens[bb] + kBS - 1) / kBS : 0;
+        const int incl = wave_incl_scan_i(n);
+        const unsigned long long hit = __ballot(bb < B && cum + incl > start);
+        if (hit) {
+            const int ln = __builtin_ctzll(hit);
+            b = c0 + ln;
+            cum += __builtin_amdgcn_readlane(incl - n, ln);
+            break;
+        }
+        cum += __builtin_amdgcn_readlane(incl, 63);
+    }
+
+    const size_t slots = (size_t)gridDim.x + B;  // the merge's piece_slots
+    int2* info = reinterpret_cast<int2*>(a.piece_info);
+    for (int pos = start; pos < end && b < B; ++b) {
+        const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+        const int n = (L + kBS - 1) / kBS;
+        if (n == 0) continue;  // an empty sequence owns no unit (the merge writes its zeros)
+        const int seg_end = min(end, cum + n);
+        const int s_first = owner(cum, W, S), s_last = owner(cum + n - 1, W, S);
+        if (h == 0 && s == s_first && threadIdx.x == 0)
+            info[b] = make_int2(s_first + b, s_last - s_first + 1);
+        RangeOut dst;
+        dst.direct = s_first == s_last;
+        dst.prow_base = (((size_t)h * slots) + (size_t)(s + b)) * cols;
+        dst.prow_stride = 0;
+        attend_range<D, KIND, MQ, WAVES>(a, b, h, L, pos - cum, seg_end - cum, dst, smem);
+        __syncthreads();  // the next piece reuses the combine LDS
+        pos = seg_end;
+        cum += n;
+    }
 }
 
 #ifndef PA_DECODE_WAVES
@@ -270,8 +416,54 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, int KIND, bool MQ>
 hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
+    if (a.balanced) {
+        dim3 grid((unsigned)a.grid_parts, (unsigned)a.num_kv_heads);
+        hipLaunchKernelGGL((decode_balanced_kernel<D, KIND, MQ, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
+        return hipGetLastError();
+    }
     return a.partition_blocks > 0 ? launch_t<D, KIND, true, MQ>(a, s)
                                   : launch_t<D, KIND, false, MQ>(a, s);
+}
+
+// Balanced splits per kv-head: the workgroups of the balanced kernel that
+// the device holds at once (occupancy x compute units), shared by the
+// kv-heads, at most kMaxBalancedSplits.  Cached per device and variant.
+template <int D, int KIND, bool MQ>
+int splits_t(int num_kv_heads) {
+    constexpr int kDevices = 64;
+    static int resident[kDevices];  // 0 = not yet known; a racing first call stores the same value
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    int total = dev < kDevices ? resident[dev] : 0;
+    if (total == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return -1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, decode_balanced_kernel<D, KIND, MQ, kWaves>, 64 * kWaves, 0) != hipSuccess)
+            return -1;
+#ifdef PA_BALANCED_PER_CU
+        per_cu = PA_BALANCED_PER_CU;  // build-time override of the occupancy
+#endif
+        total = cus * (per_cu > 0 ? per_cu : 1);
+        if (dev < kDevices) resident[dev] = total;
+    }
+    const int sp = total / num_kv_heads;
+    return sp < 1 ? 1 : (sp > kMaxBalancedSplits ? kMaxBalancedSplits : sp);
+}
+
+template <int D, int KIND>
+int splits_kind(const DecodeArgs& a) {
+    return a.q_len > 1 ? splits_t<D, KIND, true>(a.num_kv_heads) : splits_t<D, KIND, false>(a.num_kv_heads);
+}
+
+template <int D>
+int splits_d(const DecodeArgs& a) {
+    switch (a.kv_dtype) {
+        case 0: return splits_kind<D, KV_F32>(a);
+        case 1: return splits_kind<D, KV_BF16>(a);
+        default: return splits_kind<D, KV_FP8>(a);
+    }
 }
 
 template <int D, int KIND>
@@ -289,6 +481,10 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int balanced_splits(const DecodeArgs& a) {
+    return a.head_dim == 64 ? splits_d<64>(a) : splits_d<128>(a);
+}
 
 int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.num_seqs == 0) return 0;

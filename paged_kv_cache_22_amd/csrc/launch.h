@@ -28,7 +28,9 @@ struct DecodeArgs {
     int q_len;            // queries per sequence (the newest q_len cached tokens), q_len * G <= 16
     int max_blocks_per_seq;
     int partition_blocks; // blocks per partition; 0 = whole sequence in one pass
-    int grid_parts;       // partitions in the grid (1 in one-pass mode)
+    int grid_parts;       // partitions in the grid (1 in one-pass mode); balanced: splits per kv-head
+    int balanced;         // balanced split-KV: grid (splits, kv-heads), partials by piece slot
+    void* piece_info;     // balanced: int2 [num_seqs] = (first piece slot, piece count)
     float scale;
 };
 
@@ -42,6 +44,12 @@ struct MergeArgs {
     int partition_size, max_parts;
     int num_seqs, num_q_heads, head_dim;
     int skip_single;      // leave sequences with exactly one partition untouched
+    // balanced split-KV pieces (instead of partition_size / max_parts):
+    // partial row of (kv-head h, slot, column) = (h * piece_slots + slot) * cols + column
+    const void* piece_info;  // int2 [num_seqs] = (first slot, count); NULL: partition mode
+    int piece_slots;      // splits per kv-head + num_seqs
+    int q_len;            // queries per sequence; num_q_heads then counts its q_len * heads rows
+    int num_kv_heads;
 };
 
 struct PrefillArgs {
@@ -75,6 +83,14 @@ struct WriteArgs {
     int in_dtype, kv_dtype;   // pa_dtype
     int num_tokens, num_kv_heads, head_dim, num_blocks;
 };
+
+// Upper bound of the balanced split-KV splits per kv-head.
+constexpr int kMaxBalancedSplits = 1024;
+
+// Balanced splits per kv-head for these arguments on the current device
+// (occupancy of the balanced kernel x compute units / kv-heads, clamped to
+// [1, kMaxBalancedSplits]); -1 if the runtime cannot tell.
+int balanced_splits(const DecodeArgs& a);
 
 // Each returns 0 on success or the hipError_t of a failed launch.
 int launch_decode(const DecodeArgs& a, void* stream);

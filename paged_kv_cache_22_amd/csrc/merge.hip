@@ -1,4 +1,7 @@
 // Log-sum-exp merge of split-KV decode partials.  gfx950 / CDNA4.
+// Partials come either from fixed-size partitions ([row][partition]) or from
+// the balanced split's pieces (a sequence's pieces at consecutive slots,
+// (first slot, count) recorded by the decode kernel).
 //
 // Partition p of a sequence yields o_p (softmax-normalised over its tokens)
 // and lse_p = ln sum exp(s) over the same tokens.  Attention over the union of
@@ -24,13 +27,30 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     const int b = blockIdx.x / Hq;
     const size_t row = (size_t)b * Hq + qh;
     const int L = a.seq_lens[b];
-    const int np = min((L + a.partition_size - 1) / a.partition_size, a.max_parts);
+    // partials of this row: np of them at partial rows base + p * pstride
+    int np;
+    size_t base, pstride;
+    if (a.piece_info) {
+        // balanced pieces: row qh' = qi * H + qh of the sequence (H real heads)
+        const int H = Hq / a.q_len, G = H / a.num_kv_heads;
+        const int qi = qh / H, hq = qh - qi * H;
+        const int h = hq / G, col = qi * G + (hq - h * G);
+        const size_t cols = (size_t)a.q_len * G;
+        const int2 info = L > 0 ? reinterpret_cast<const int2*>(a.piece_info)[b] : make_int2(0, 0);
+        np = info.y;
+        base = ((size_t)h * a.piece_slots + info.x) * cols + col;
+        pstride = cols;
+    } else {
+        np = min((L + a.partition_size - 1) / a.partition_size, a.max_parts);
+        base = row * a.max_parts;
+        pstride = 1;
+    }
     if (a.skip_single && np == 1) return;  // written by the partition kernel
-    const float* lse = a.part_lse + row * a.max_parts;
-    const float* po = a.part_out + row * a.max_parts * D + lane * V;
+    const float* lse = a.part_lse + base;
+    const float* po = a.part_out + base * D + lane * V;
 
     float M = -INFINITY;
-    for (int p = lane; p < np; p += 64) M = fmaxf(M, lse[p]);
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, lse[(size_t)p * pstride]);
     M = wave_max(M);
 
     float acc[V];
@@ -42,10 +62,10 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         for (int p = 0; p < np; ++p) {
             // difference first: exactly 0 for the largest lse, whatever the
             // compiler fuses, so a lone partition passes through unchanged
-            const float w = fast_exp2((lse[p] - M) * kLog2e);
+            const float w = fast_exp2((lse[(size_t)p * pstride] - M) * kLog2e);
             den += w;
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[v] += w * po[(size_t)p * D + v];
+            for (int v = 0; v < V; ++v) acc[v] += w * po[(size_t)p * pstride * D + v];
         }
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;

@@ -223,3 +223,36 @@ def test_multi_query_rejects():
     assert call(B=0, out=None, q=None, ws=None) == OK
     need = pa.decode_workspace_size(64, 4 * 32, 128, 4096, 512)
     assert call(wsb=need - 1) == WS
+
+
+def test_balanced_mode_arguments():
+    bal = pa.PA_PARTITION_BALANCED
+    assert bal == -1
+    slots = 1024 + 64
+    want = (-(-64 * 8 // 256) * 256 + -(-slots * 32 * 128 * 4 // 256) * 256
+            + -(-slots * 32 * 4 // 256) * 256)
+    assert pa.decode_workspace_size(64, 32, 128, 4096, bal) == want
+    assert decode_call(part=bal, ws=None) == WS
+    assert decode_call(part=bal, ws_bytes=want - 1) == WS
+    assert decode_call(part=-2) == SHAPE
+    assert decode_call(part=bal, num_seqs=0, out=None, q=None, ws=None) == OK
+    f = pa.lib.pa_decode_partitions
+    assert f(P, P, 8, P, 1, P, P, 1, P, 256, P, 64, 32, 8, 128, 16, 9000, 0.08, None, None,
+             bal, 4096, None) == UNSUP
+
+
+def test_stages_rejects():
+    f = pa.lib.pa_decode_stages
+
+    def call(**over):
+        a = dict(out=P, q=P, qd=1, qn=1, k=P, v=P, kvd=1, bt=P, mb=256, sl=P, B=64, hq=32, hkv=8,
+                 d=128, bs=16, nb=9000, scale=0.088, ks=None, vs=None, part=512, max_len=4096,
+                 ws=P, wsb=1 << 30, stages=3, stream=None)
+        a.update(over)
+        return f(*a.values())
+
+    assert call(stages=0) == SHAPE
+    assert call(stages=4) == SHAPE
+    assert call(qn=8) == UNSUP                    # 8 x 4 columns: only the prefill route has them
+    assert call(qn=0) == SHAPE
+    assert call(ws=None) == WS
