@@ -142,9 +142,9 @@ def test_quantiser_maps_amax_to_448():
 # ---------------------------------------------------------------------------
 # P1: dense library routine (decode and prefill, GQA)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_decode_matches_dense_sdpa(seed):
-    q, Ks, Vs, kp, vp, table, lens = rand_decode_case(seed)
+@pytest.mark.parametrize("seed,bs", [(0, 16), (1, 16), (2, 16), (3, 32), (4, 64)])
+def test_decode_matches_dense_sdpa(seed, bs):
+    q, Ks, Vs, kp, vp, table, lens = rand_decode_case(seed, bs=bs)
     B, Hq, d = q.shape
     Hkv = kp.shape[1]
     G = Hq // Hkv
@@ -178,10 +178,10 @@ def bottom_right_mask(n, L):
     return np.arange(L)[None, :] <= (ctx + np.arange(n))[:, None]
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_prefill_matches_dense_sdpa_bottom_right(seed):
+@pytest.mark.parametrize("seed,bs", [(0, 16), (1, 16), (2, 32), (3, 64)])
+def test_prefill_matches_dense_sdpa_bottom_right(seed, bs):
     q_lens, ctx_lens = [5, 17, 40], [0, 33, 9]
-    q, cu, Ks, Vs, kp, vp, table, lens = _prefill_case(seed, q_lens, ctx_lens)
+    q, cu, Ks, Vs, kp, vp, table, lens = _prefill_case(seed, q_lens, ctx_lens, bs=bs)
     Hq, d = q.shape[1], q.shape[2]
     G = Hq // kp.shape[1]
     scale = 1.0 / math.sqrt(d)
@@ -295,6 +295,25 @@ def test_merge_closed_forms():
 # ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
+def test_block_size_invariance():
+    """The same token rows paged with 16-, 32- and 64-token blocks: the
+    oracle's decode and prefill results are bit-identical."""
+    rng = np.random.default_rng(9)
+    Ls = [1, 16, 17, 63, 64, 65, 200]
+    Ks = [rng.standard_normal((L, 2, 16)) for L in Ls]
+    Vs = [rng.standard_normal((L, 2, 16)) for L in Ls]
+    q = f32(rng.standard_normal((len(Ls), 8, 16)))
+    cu = np.arange(len(Ls) + 1, dtype=np.int32)             # one query per sequence
+    outs = []
+    for bs in (16, 32, 64):
+        kp, vp, table, lens = scatter_to_pages(Ks, Vs, bs, np.random.default_rng(bs))
+        dec, _ = oracle.decode(q, f32(kp), f32(vp), table, lens, 0.25, "f32", "f32")
+        pre, _ = oracle.prefill_chunk(q, cu, f32(kp), f32(vp), table, lens, 0.25, "f32", "f32")
+        outs.append((dec, pre))
+    for dec, pre in outs[1:]:
+        assert (dec == outs[0][0]).all() and (pre == outs[0][1]).all()
+
+
 def test_physical_permutation_invariance():
     wl = W.decode_workload(seed=21, num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=32,
                            len_lo=1, len_hi=90, q_dtype="bf16", kv_dtype="bf16", pool_blocks=40)
@@ -420,8 +439,10 @@ def test_config4_prefix_is_shared():
 # ---------------------------------------------------------------------------
 def _pins_pass():
     try:
-        test_decode_matches_dense_sdpa(0)
-        test_prefill_matches_dense_sdpa_bottom_right(0)
+        test_decode_matches_dense_sdpa(0, 16)
+        test_decode_matches_dense_sdpa(4, 64)
+        test_prefill_matches_dense_sdpa_bottom_right(0, 16)
+        test_prefill_matches_dense_sdpa_bottom_right(3, 64)
         test_split_equals_unsplit(16)
         test_uniform_scores_give_mean_of_v(17)
         test_equal_keys_at_huge_logits_give_mean_of_v()
