@@ -33,7 +33,10 @@
  *   partial_out        fp32 [num_seqs, num_q_heads, max_partitions, head_dim]
  *   partial_lse        fp32 [num_seqs, num_q_heads, max_partitions], natural log
  *
- * Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ * Supported: head_dim 64 or 128; block_size 16, 32 or 64 (vllm-mblt 0.8.0,
+ * "Chunked Prefill Auto-Tuning": a 64-token block size as an override of the
+ * default);
+ * num_q_heads a multiple of
  * num_kv_heads with G <= 16; dtypes (q, kv) = (F32, F32), (BF16, BF16) or
  * (BF16, FP8_E4M3); out has q's dtype; q, out, k_cache, v_cache 16-byte
  * aligned.
@@ -113,7 +116,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * cache) attends to keys 0 .. seq_lens[b]-1.
  *
  * partition_size == 0: one pass per (sequence, kv-head), out written
- * directly.  partition_size > 0 (a multiple of block_size): split-KV; each
+ * directly.  partition_size > 0 (a multiple of 16 tokens): split-KV; each
  * partition p covers tokens [p*P, min((p+1)*P, L)) and writes its normalised
  * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
  * pa_merge_partitions) writes out.  A sequence that fits in one partition

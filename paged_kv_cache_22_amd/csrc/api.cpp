@@ -11,7 +11,9 @@
 
 namespace {
 
-constexpr int kBlockSize = 16;
+constexpr int kUnit = 16;             // tokens per kernel unit; partitions are whole units
+
+bool block_size_ok(int bs) { return bs == 16 || bs == 32 || bs == 64; }
 constexpr int kMaxGroup = 16;          // q-heads per kv-head handled by one wave
 constexpr int kMaxGridY = 65535;
 constexpr size_t kRegionAlign = 256;
@@ -45,7 +47,7 @@ int common_checks(const void* q, const void* k_cache, const void* v_cache, int q
     if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
     if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return PA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
@@ -66,7 +68,7 @@ int decode_checks(const void* q, int q_dtype, const void* k_cache, const void* v
     if ((long long)num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
     if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
     if (partition_size < 0 && partition_size != PA_PARTITION_BALANCED) return PA_ERR_SHAPE;
-    if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_UNSUPPORTED;
+    if (partition_size > 0 && partition_size % kUnit != 0) return PA_ERR_UNSUPPORTED;
     if (partition_size > 0) {
         const long long parts = ((long long)max_seq_len + partition_size - 1) / partition_size;
         if (parts > kMaxGridY) return PA_ERR_UNSUPPORTED;
@@ -77,9 +79,10 @@ int decode_checks(const void* q, int q_dtype, const void* k_cache, const void* v
 pa::DecodeArgs make_decode_args(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
                                 int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
                                 const int32_t* seq_lens, int num_seqs, int num_q_heads,
-                                int num_kv_heads, int head_dim, float scale, const float* k_scale,
-                                const float* v_scale) {
+                                int num_kv_heads, int head_dim, int block_size, float scale,
+                                const float* k_scale, const float* v_scale) {
     pa::DecodeArgs a{};
+    a.block_size = block_size;
     a.q = q;
     a.q_dtype = q_dtype;
     a.k_cache = k_cache;
@@ -158,11 +161,11 @@ int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partiti
     if (num_seqs == 0 || parts == 0) return PA_OK;
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
                                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
-                                        num_kv_heads, head_dim, scale, k_scale, v_scale);
+                                        num_kv_heads, head_dim, block_size, scale, k_scale, v_scale);
     a.part_out = partial_out;
     a.part_lse = partial_lse;
     a.max_parts = max_partitions;
-    a.partition_blocks = partition_size / block_size;
+    a.partition_blocks = partition_size / kUnit;
     a.grid_parts = parts;
     return hip_status(pa::launch_decode(a, stream));
 }
@@ -204,14 +207,14 @@ namespace {
 int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
                 const void* v_cache, int kv_dtype, const int32_t* block_table,
                 int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
-                int num_kv_heads, int head_dim, float scale, const float* k_scale,
+                int num_kv_heads, int head_dim, int block_size, float scale, const float* k_scale,
                 const float* v_scale, int partition_size, int max_seq_len, void* workspace,
                 size_t workspace_bytes, void* stream, int stages = PA_STAGE_ALL) {
     const bool run_attn = stages & PA_STAGE_ATTENTION, run_merge = stages & PA_STAGE_MERGE;
     const int rows_per_seq = q_len * num_q_heads;   // output rows of one sequence
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
                                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
-                                        num_kv_heads, head_dim, scale, k_scale, v_scale);
+                                        num_kv_heads, head_dim, block_size, scale, k_scale, v_scale);
     a.q_len = q_len;
     if (partition_size == 0) {
         if (num_seqs == 0) return PA_OK;
@@ -274,7 +277,7 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
     a.part_lse = reinterpret_cast<float*>(ws + off_lse);
     a.single_direct = 1;
     a.max_parts = parts;
-    a.partition_blocks = partition_size / kBlockSize;
+    a.partition_blocks = partition_size / kUnit;
     a.grid_parts = parts;
     int st = run_attn ? hip_status(pa::launch_decode(a, stream)) : PA_OK;
     if (st != PA_OK || !run_merge) return st;
@@ -312,7 +315,7 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
     if (!aligned16(out)) return PA_ERR_ALIGN;
     return decode_impl(out, q, q_dtype, 1, k_cache, v_cache, kv_dtype, block_table,
                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                       scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
+                       block_size, scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
                        workspace_bytes, stream);
 }
 
@@ -335,7 +338,7 @@ int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len, cons
     if ((long long)q_len * G <= kMaxGroup)
         return decode_impl(out, q, q_dtype, q_len, k_cache, v_cache, kv_dtype, block_table,
                            max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
-                           head_dim, scale, k_scale, v_scale, partition_size, max_seq_len,
+                           head_dim, block_size, scale, k_scale, v_scale, partition_size, max_seq_len,
                            workspace, workspace_bytes, stream);
     // more (query, head) pairs than MFMA columns: the prefill kernel, each
     // sequence a chunk of q_len rows (no partitions, no workspace)
@@ -361,6 +364,7 @@ int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len, cons
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
+    a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale = scale;
     return hip_status(pa::launch_prefill(a, stream));
@@ -385,7 +389,7 @@ int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len, const voi
     if ((long long)q_len * (num_q_heads / num_kv_heads) > kMaxGroup) return PA_ERR_UNSUPPORTED;
     return decode_impl(out, q, q_dtype, q_len, k_cache, v_cache, kv_dtype, block_table,
                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                       scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
+                       block_size, scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
                        workspace_bytes, stream, stages);
 }
 
@@ -428,6 +432,7 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, cons
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
+    a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale = scale;
     return hip_status(pa::launch_prefill(a, stream));
@@ -446,7 +451,7 @@ int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype, const void* key, con
     if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
         return PA_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+    if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
     const long long row = (long long)num_kv_heads * head_dim;
     if (key_stride < row || value_stride < row) return PA_ERR_SHAPE;
     if ((long long)num_blocks * block_size > 0x7fffffffLL) return PA_ERR_SHAPE;
@@ -478,6 +483,7 @@ int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype, const void* key, con
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
     a.num_blocks = num_blocks;
+    a.block_size = block_size;
     return hip_status(pa::launch_write_kv(a, stream));
 }
 

@@ -40,6 +40,8 @@
 #include "launch.h"
 #include "tiles.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -56,10 +58,11 @@ struct RangeOut {
 // Attention of sequence b (L cached tokens), kv-head h, over its logical
 // blocks [j0, j1) by the workgroup's WAVES waves (j0 < j1).  Wave w takes
 // blocks j0 + w, j0 + w + WAVES, ...; wave 0 combines and writes.
-template <int D, int KIND, bool MQ, int WAVES>
+template <int D, int KIND, int BS, bool MQ, int WAVES>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, int L, int j0, int j1,
                                              const RangeOut& dst, float* smem) {
-    using T = Tile<KIND, D>;
+    using T = Tile<KIND, D, BS>;
+    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
 
@@ -90,12 +93,14 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;  // raw score -> base-2 logit (C > 0)
 
-    // block-table window of this wave: lane i holds the entry of its block
-    // number tbase + i (and tbase + 64 + i in tnxt)
-    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0 + w;
+    // block-table window of this wave: lane i holds the table entry of its
+    // unit number tbase + i (and tbase + 64 + i in tnxt); unit u of the
+    // sequence lies in block u / (BS / 16)
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq;
+    const int ubase = j0 + w;  // the wave's unit i is ubase + i * WAVES
     int tbase = 0;
-    int tcur = (lane < n_mine) ? trow[lane * WAVES] : 0;
-    int tnxt = (64 + lane < n_mine) ? trow[(64 + lane) * WAVES] : 0;
+    int tcur = (lane < n_mine) ? trow[(ubase + lane * WAVES) >> kSubShift] : 0;
+    int tnxt = (64 + lane < n_mine) ? trow[(ubase + (64 + lane) * WAVES) >> kSubShift] : 0;
 
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
@@ -106,7 +111,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
         const int phys = idx < 64 ? __builtin_amdgcn_readlane(tcur, idx)
                                   : __builtin_amdgcn_readlane(tnxt, idx - 64);
         const size_t off = (size_t)phys * blk_stride;
-        T::load(R, kbase + off, vbase + off, r, c);
+        const int sub = (ubase + i * WAVES) & ((1 << kSubShift) - 1);  // unit within the block
+        T::load(R, kbase + off + sub * T::kUnitK, vbase + off + sub * T::kUnitV, r, c);
     };
 
     float m = -INFINITY, l = 0.f;
@@ -172,7 +178,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
             if (i - tbase >= 64) {  // slide the table window (uniform, once per 64 blocks)
                 tbase += 64;
                 tcur = tnxt;
-                tnxt = (tbase + 64 + lane < n_mine) ? trow[(tbase + 64 + lane) * WAVES] : 0;
+                tnxt = (tbase + 64 + lane < n_mine) ? trow[(ubase + (tbase + 64 + lane) * WAVES) >> kSubShift] : 0;
             }
             issue(b1, i + 1);
             consume(b0, i);
@@ -281,7 +287,7 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int b, int h) {
 
 // One workgroup per (sequence, kv-head, partition): the one-pass mode
 // (SPLIT = false, one partition) and the fixed-size split-KV mode.
-template <int D, int KIND, bool SPLIT, bool MQ, int WAVES>
+template <int D, int KIND, int BS, bool SPLIT, bool MQ, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) {
     __shared__ float smem[combine_floats<D, KIND, WAVES>()];
     const int Hkv = a.num_kv_heads;
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     dst.direct = !SPLIT || (np == 1 && a.single_direct);
     dst.prow_base = (size_t)part;
     dst.prow_stride = (size_t)a.max_parts;
-    attend_range<D, KIND, MQ, WAVES>(a, b, h, L, j0, j1, dst, smem);
+    attend_range<D, KIND, BS, MQ, WAVES>(a, b, h, L, j0, j1, dst, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,7 +346,7 @@ __device__ __forceinline__ int owner(long long x, long long W, int S) {
     return (int)(((x + 1) * S - 1) / W);
 }
 
-template <int D, int KIND, bool MQ, int WAVES>
+template <int D, int KIND, int BS, bool MQ, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const DecodeArgs a) {
     __shared__ float smem[combine_floats<D, KIND, WAVES>()];
     const int lane = threadIdx.x & 63;
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
         dst.direct = s_first == s_last;
         dst.prow_base = (((size_t)h * slots) + (size_t)(s + b)) * cols;
         dst.prow_stride = 0;
-        attend_range<D, KIND, MQ, WAVES>(a, b, h, L, pos - cum, seg_end - cum, dst, smem);
+        attend_range<D, KIND, BS, MQ, WAVES>(a, b, h, L, pos - cum, seg_end - cum, dst, smem);
         __syncthreads();  // the next piece reuses the combine LDS
         pos = seg_end;
         cum += n;
@@ -406,29 +412,30 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;
 
-template <int D, int KIND, bool SPLIT, bool MQ>
+template <int D, int KIND, int BS, bool SPLIT, bool MQ>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), SPLIT ? (unsigned)a.grid_parts : 1u);
-    hipLaunchKernelGGL((decode_kernel<D, KIND, SPLIT, MQ, kWaves>), grid,
+    hipLaunchKernelGGL((decode_kernel<D, KIND, BS, SPLIT, MQ, kWaves>), grid,
                        dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 
-template <int D, int KIND, bool MQ>
+template <int D, int KIND, int BS, bool MQ>
 hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
     if (a.balanced) {
         dim3 grid((unsigned)a.grid_parts, (unsigned)a.num_kv_heads);
-        hipLaunchKernelGGL((decode_balanced_kernel<D, KIND, MQ, kWaves>), grid, dim3(64 * kWaves), 0, s, a);
+        hipLaunchKernelGGL((decode_balanced_kernel<D, KIND, BS, MQ, kWaves>), grid, dim3(64 * kWaves),
+                           0, s, a);
         return hipGetLastError();
     }
-    return a.partition_blocks > 0 ? launch_t<D, KIND, true, MQ>(a, s)
-                                  : launch_t<D, KIND, false, MQ>(a, s);
+    return a.partition_blocks > 0 ? launch_t<D, KIND, BS, true, MQ>(a, s)
+                                  : launch_t<D, KIND, BS, false, MQ>(a, s);
 }
 
 // Balanced splits per kv-head: the workgroups of the balanced kernel that
 // the device holds at once (occupancy x compute units), shared by the
 // kv-heads, at most kMaxBalancedSplits.  Cached per device and variant.
-template <int D, int KIND, bool MQ>
+template <int D, int KIND, int BS, bool MQ>
 int splits_t(int num_kv_heads) {
     constexpr int kDevices = 64;
     static int resident[kDevices];  // 0 = not yet known; a racing first call stores the same value
@@ -440,7 +447,7 @@ int splits_t(int num_kv_heads) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return -1;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, decode_balanced_kernel<D, KIND, MQ, kWaves>, 64 * kWaves, 0) != hipSuccess)
+                &per_cu, decode_balanced_kernel<D, KIND, BS, MQ, kWaves>, 64 * kWaves, 0) != hipSuccess)
             return -1;
 #ifdef PA_BALANCED_PER_CU
         per_cu = PA_BALANCED_PER_CU;  // build-time override of the occupancy
@@ -452,45 +459,52 @@ int splits_t(int num_kv_heads) {
     return sp < 1 ? 1 : (sp > kMaxBalancedSplits ? kMaxBalancedSplits : sp);
 }
 
-template <int D, int KIND>
-int splits_kind(const DecodeArgs& a) {
-    return a.q_len > 1 ? splits_t<D, KIND, true>(a.num_kv_heads) : splits_t<D, KIND, false>(a.num_kv_heads);
+// one dispatch over (head_dim, kv dtype, block size, multi-query): F is
+// called with the matching template arguments
+template <class F>
+auto dispatch(const DecodeArgs& a, F&& f) {
+    auto by_bs = [&](auto d, auto kind) {
+        constexpr int D = decltype(d)::value, K = decltype(kind)::value;
+        auto by_mq = [&](auto bs) {
+            constexpr int BS = decltype(bs)::value;
+            return a.q_len > 1 ? f.template operator()<D, K, BS, true>()
+                               : f.template operator()<D, K, BS, false>();
+        };
+        if (a.block_size == 64) return by_mq(std::integral_constant<int, 64>{});
+        if (a.block_size == 32) return by_mq(std::integral_constant<int, 32>{});
+        return by_mq(std::integral_constant<int, 16>{});
+    };
+    auto by_kind = [&](auto d) {
+        switch (a.kv_dtype) {
+            case 0: return by_bs(d, std::integral_constant<int, KV_F32>{});
+            case 1: return by_bs(d, std::integral_constant<int, KV_BF16>{});
+            default: return by_bs(d, std::integral_constant<int, KV_FP8>{});
+        }
+    };
+    return a.head_dim == 64 ? by_kind(std::integral_constant<int, 64>{})
+                            : by_kind(std::integral_constant<int, 128>{});
 }
 
-template <int D>
-int splits_d(const DecodeArgs& a) {
-    switch (a.kv_dtype) {
-        case 0: return splits_kind<D, KV_F32>(a);
-        case 1: return splits_kind<D, KV_BF16>(a);
-        default: return splits_kind<D, KV_FP8>(a);
-    }
-}
+struct LaunchF {
+    const DecodeArgs& a;
+    hipStream_t s;
+    template <int D, int K, int BS, bool MQ>
+    hipError_t operator()() const { return launch_mq<D, K, BS, MQ>(a, s); }
+};
 
-template <int D, int KIND>
-hipError_t launch_kind(const DecodeArgs& a, hipStream_t s) {
-    return a.q_len > 1 ? launch_mq<D, KIND, true>(a, s) : launch_mq<D, KIND, false>(a, s);
-}
-
-template <int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-    switch (a.kv_dtype) {
-        case 0: return launch_kind<D, KV_F32>(a, s);
-        case 1: return launch_kind<D, KV_BF16>(a, s);
-        default: return launch_kind<D, KV_FP8>(a, s);
-    }
-}
+struct SplitsF {
+    const DecodeArgs& a;
+    template <int D, int K, int BS, bool MQ>
+    int operator()() const { return splits_t<D, K, BS, MQ>(a.num_kv_heads); }
+};
 
 }  // namespace
 
-int balanced_splits(const DecodeArgs& a) {
-    return a.head_dim == 64 ? splits_d<64>(a) : splits_d<128>(a);
-}
+int balanced_splits(const DecodeArgs& a) { return dispatch(a, SplitsF{a}); }
 
 int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.num_seqs == 0) return 0;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = a.head_dim == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
-    return (int)e;
+    return (int)dispatch(a, LaunchF{a, reinterpret_cast<hipStream_t>(stream)});
 }
 
 }  // namespace pa

@@ -25,6 +25,7 @@ struct DecodeArgs {
     int q_dtype;          // pa_dtype
     int kv_dtype;         // pa_dtype
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int block_size;       // tokens per cache block: 16, 32 or 64
     int q_len;            // queries per sequence (the newest q_len cached tokens), q_len * G <= 16
     int max_blocks_per_seq;
     int partition_blocks; // blocks per partition; 0 = whole sequence in one pass
@@ -66,6 +67,7 @@ struct PrefillArgs {
     const float* v_scale;
     int q_dtype, kv_dtype;
     int num_chunks, num_q_heads, num_kv_heads, head_dim;
+    int block_size;       // tokens per cache block: 16, 32 or 64
     int uniform_q_len;    // > 0: chunk c owns rows c*uniform_q_len .. (cu_q_lens unused)
     int max_blocks_per_seq;
     float scale;
@@ -82,6 +84,7 @@ struct WriteArgs {
     long long key_stride, value_stride;   // elements between consecutive tokens
     int in_dtype, kv_dtype;   // pa_dtype
     int num_tokens, num_kv_heads, head_dim, num_blocks;
+    int block_size;           // tokens per cache block: 16, 32 or 64
 };
 
 // Upper bound of the balanced split-KV splits per kv-head.

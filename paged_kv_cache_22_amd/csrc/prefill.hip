@@ -30,12 +30,14 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kStepBlocks = 2;  // key blocks per LDS stage (consumed as a pair)
 
-template <int D, int KIND, int NC>
+template <int D, int KIND, int BS, int NC>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
-    using T = Tile<KIND, D>;
+    using T = Tile<KIND, D, BS>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
-    constexpr int TB = T::kTileBytes;                       // one K (or V) tile in HBM
+    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
+    constexpr int TB = T::kUnitBytes;                       // one 16-token K (or V) unit
+    constexpr int kUnitRun = kBS * 16;                       // one K chunk run of a unit
     constexpr int kVLds = D * T::kVRowLds;                   // one V tile in LDS (padded rows)
     constexpr int kSlot = (TB + kVLds + 15) / 16 * 16;       // K then V of one block
     constexpr int kPieces = kStepBlocks * 2 * TB / 16;       // 16-byte pieces per step
@@ -98,13 +100,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;
 
-    // block-table window (every wave holds the same 64 entries)
+    // block-table window (every wave holds the same 64 entries): lane i holds
+    // the table entry of unit tbase + i, unit u lying in block u / (BS / 16)
     const int32_t* trow = a.block_table + (size_t)ch * a.max_blocks_per_seq;
     int tbase = 0;
-    int tcur = (lane < nblk) ? trow[lane] : 0;
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * TB;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * TB;
-    const size_t blk_stride = (size_t)Hkv * TB;
+    int tcur = (lane < nblk) ? trow[lane >> kSubShift] : 0;
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
+    const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
 
     // global -> registers for one step: piece p is byte 16 * (p % (TB/16)) of
     // tile p / (TB/16) = (block of the step, K or V)
@@ -116,7 +119,13 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
             const int jb = min(j0 + (tile >> 1), nblk - 1);  // a missing 2nd block re-reads the 1st
             const int phys = __shfl(tcur, jb - tbase, 64);
-            const char* src = ((tile & 1) ? vbase : kbase) + (size_t)phys * blk_stride + off;
+            const int sub = jb & ((1 << kSubShift) - 1);    // unit within the block
+            // the piece's place in the block's tile: K chunk runs and V rows
+            // are BS tokens long, the unit's 16 tokens at offset 16 * sub
+            const int goff = (tile & 1)
+                ? (off / T::kVRow) * T::kVRow * (BS / kBS) + sub * T::kUnitV + off % T::kVRow
+                : (off / kUnitRun) * kUnitRun * (BS / kBS) + sub * T::kUnitK + off % kUnitRun;
+            const char* src = ((tile & 1) ? vbase : kbase) + (size_t)phys * blk_stride + goff;
             held[u] = ld16(src);
         }
     };
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         if (s + 1 < nsteps) {
             if (j0 + 2 * kStepBlocks - 1 - tbase >= 64) {  // next step leaves the table window
                 tbase += 64 - kStepBlocks;                  // keep the 2 steps in one window
-                tcur = (tbase + lane < nblk) ? trow[tbase + lane] : 0;
+                tcur = (tbase + lane < nblk) ? trow[(tbase + lane) >> kSubShift] : 0;
             }
             fetch(j0 + kStepBlocks);  // in flight during this step's compute
         }
@@ -239,22 +248,29 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
 #endif
 constexpr int kNC = PA_PREFILL_NC;
 
-template <int D, int KIND>
+template <int D, int KIND, int BS>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const long rows = (long)a.max_q_len * G;
     const long per_wg = 16L * kNC * kWaves;
     dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + per_wg - 1) / per_wg));
-    hipLaunchKernelGGL((prefill_kernel<D, KIND, kNC>), grid, dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, KIND, BS, kNC>), grid, dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
+}
+
+template <int D, int KIND>
+hipError_t launch_kind(const PrefillArgs& a, hipStream_t s) {
+    if (a.block_size == 64) return launch_t<D, KIND, 64>(a, s);
+    if (a.block_size == 32) return launch_t<D, KIND, 32>(a, s);
+    return launch_t<D, KIND, 16>(a, s);
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
     switch (a.kv_dtype) {
-        case 0: return launch_t<D, KV_F32>(a, s);
-        case 1: return launch_t<D, KV_BF16>(a, s);
-        default: return launch_t<D, KV_FP8>(a, s);
+        case 0: return launch_kind<D, KV_F32>(a, s);
+        case 1: return launch_kind<D, KV_BF16>(a, s);
+        default: return launch_kind<D, KV_FP8>(a, s);
     }
 }
 

@@ -1,9 +1,11 @@
 // Per-KV-dtype access to one (block, kv-head) tile of the paged cache, in the
 // MFMA operand layouts the attention kernels use.  gfx950 / CDNA4.
 //
-// A K tile is [D*eb/16 chunks][16 tokens][16 bytes]: 16-byte chunks of
+// A K tile is [D*eb/16 chunks][BS tokens][16 bytes]: 16-byte chunks of
 // consecutive dims with the token index inside each chunk.  A V tile is
-// [D][16 tokens] (dim-major).  Both products of attention then read their
+// [D][BS tokens] (dim-major).  BS, the cache block size, is 16, 32 or 64;
+// the kernels work in 16-token units, unit u of a block starting 16u tokens
+// into each K chunk run and each V row.  Both products of attention then read their
 // MFMA operands as whole contiguous runs: for the score product
 // S^T = K . Q^T (contraction over dims) lane (r, c) takes chunk 4i + c of
 // token r, so one load instruction of the wave reads 1 KiB in one piece; for
@@ -16,20 +18,23 @@
 
 namespace pa {
 
-constexpr int kBS = 16;  // tokens per cache block
+constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hold 1, 2 or 4 units
 
 // ---------------------------------------------------------------------------
 // Per-KV-dtype tile access.  For every kind:
 //   Regs  the lane's share of one block's K and V tile
 //   QOp   the lane's share of Q^T, the B operand of the score MFMAs
-//   load  issues the global loads of one block
+//   load  issues the global loads of one 16-token unit (kt, vt: the unit's
+//         start; BS: the block's token count, the K chunk and V row stride)
 //   qk    S^T fragment: lane (r, c) gets scores of head r, tokens 4c..4c+3
 //   pv    acc[n] += V^T[16n..16n+15, tokens] . P^T for this block
 // ---------------------------------------------------------------------------
-template <int KIND, int D> struct Tile;
+template <int KIND, int D, int BS = kBS> struct Tile;
 
-template <int D> struct Tile<KV_BF16, D> {
-    static constexpr int kTileBytes = kBS * D * 2;
+template <int D, int BS> struct Tile<KV_BF16, D, BS> {
+    static constexpr int kTileBytes = BS * D * 2;     // one (block, kv-head) tile
+    static constexpr int kUnitBytes = kBS * D * 2;    // one 16-token unit
+    static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 2;  // unit offsets in K runs / V rows
     static constexpr int KL = D / 32;  // 16-byte K loads per lane = score MFMAs
     static constexpr int NT = D / 16;  // 16-dim tiles of the output
     struct Regs { u32x4 k[KL]; u32x2 v[NT]; };
@@ -43,9 +48,9 @@ template <int D> struct Tile<KV_BF16, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (kBS * 2) + c * 8);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (BS * 2) + c * 8);
     }
     // the same lane layout read from a tile staged in LDS (plain loads)
     // V rows in LDS are kVRowLds bytes apart (padded: conflict-free reads)
@@ -87,8 +92,10 @@ template <int D> struct Tile<KV_BF16, D> {
     }
 };
 
-template <int D> struct Tile<KV_FP8, D> {
-    static constexpr int kTileBytes = kBS * D;
+template <int D, int BS> struct Tile<KV_FP8, D, BS> {
+    static constexpr int kTileBytes = BS * D;
+    static constexpr int kUnitBytes = kBS * D;
+    static constexpr int kUnitK = kBS * 16, kUnitV = kBS;
     static constexpr int KL = D / 64;  // 16-byte K loads per lane, 16 codes = two MFMAs each
     static constexpr int NT = D / 16;
     struct Regs { u32x4 k[KL]; unsigned v[NT]; };
@@ -105,9 +112,9 @@ template <int D> struct Tile<KV_FP8, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * kBS + c * 4);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * BS + c * 4);
     }
     static constexpr int kVRow = kBS, kVRowLds = kVRow + 4;
     __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
@@ -153,8 +160,10 @@ template <int D> struct Tile<KV_FP8, D> {
     }
 };
 
-template <int D> struct Tile<KV_F32, D> {
-    static constexpr int kTileBytes = kBS * D * 4;
+template <int D, int BS> struct Tile<KV_F32, D, BS> {
+    static constexpr int kTileBytes = BS * D * 4;
+    static constexpr int kUnitBytes = kBS * D * 4;
+    static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 4;
     static constexpr int KL = D / 16;  // 16-byte K loads per lane, four MFMAs each
     static constexpr int NT = D / 16;
     struct Regs { u32x4 k[KL]; u32x4 v[NT]; };
@@ -168,9 +177,9 @@ template <int D> struct Tile<KV_F32, D> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (kBS * 4) + c * 16);
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (BS * 4) + c * 16);
     }
     static constexpr int kVRow = kBS * 4, kVRowLds = kVRow + 16;
     __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {

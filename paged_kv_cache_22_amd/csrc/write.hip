@@ -1,5 +1,5 @@
 // KV-cache write: the K/V rows of new tokens scattered into their cache slots
-// through a slot mapping (slot = physical block * 16 + offset), with optional
+// through a slot mapping (slot = physical block * block size + offset), with optional
 // fp8-e4m3 quantisation by a per-kv-head scale (vllm-metis 0.1.0, "Status":
 // FP8 with one scale of amax / 448; vllm-metal architecture article, section
 // 四: the cache is addressed through block tables, so a new token's position
@@ -21,7 +21,7 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBlock = 16;
+constexpr int kUnit = 16;   // tokens of a whole-unit group (one wave's 16 token rows)
 
 // cache elements per 16-byte K chunk
 template <int KV>
@@ -121,7 +121,9 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
     const int h = hc / nchunk;
     const int j = hc - h * nchunk;
     const int tbase = tg * (16 * TPL) + r;
-    const int cap = a.num_blocks * kBlock;
+    const int bs = a.block_size;          // 16, 32 or 64
+    const int bs_shift = bs == 64 ? 6 : bs == 32 ? 5 : 4;
+    const int cap = a.num_blocks * bs;
 
     // All loads first and unconditionally, so that they are all in flight
     // together: a token past the end reads the last token's row (always
@@ -151,10 +153,11 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
         const bool live = slot[i] >= 0 && slot[i] < cap;       // not padding, inside the pool
-        // Wave-uniform: are the wave's 16 tokens one whole block, in order?
-        // (lane 0 holds token r = 0; every lane group holds the same tokens)
+        // Wave-uniform: are the wave's 16 tokens one whole 16-token unit of a
+        // block, in order?  (lane 0 holds token r = 0; every lane group holds
+        // the same tokens)
         const int s0 = __builtin_amdgcn_readfirstlane(slot[i]);
-        const bool whole = __all(live && slot[i] == s0 + r) && (s0 % kBlock) == 0;
+        const bool whole = __all(live && slot[i] == s0 + r) && (s0 % kUnit) == 0;
 
         // this token's K chunk and V elements, in cache encoding
         u32x4 kw, vw;
@@ -176,35 +179,40 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
             kw = kraw[i][0];
             vw = vraw[i][0];
         }
-        const int blk = slot[i] / kBlock;
-        const int off = slot[i] - blk * kBlock;
+        const int blk = slot[i] >> bs_shift;
+        const int off = slot[i] & (bs - 1);
         const size_t tile = (size_t)blk * a.num_kv_heads + h;    // (block, kv-head) tile
         // K: chunk j of the tile, 16 bytes at token offset `off`
         if (live)
             *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) +
-                                      ((tile * nchunk + j) * kBlock + off) * 16) = kw;
+                                      ((tile * nchunk + j) * bs + off) * 16) = kw;
         if (whole) {
             // V through LDS: the wave's four chunks of the 16 tokens cover the
-            // 1 KiB run of dim rows (hc0's first dim .. +4X) of this block's tile
+            // unit's 16 * element bytes of 4X dim rows (hc0's first dim ..
+            // +4X) of this block's tile, 1 KiB in all; lane L stores 16 bytes:
+            // piece L % eb of row L / eb (eb = element bytes)
             stage[w][lane] = vw;
             __builtin_amdgcn_wave_barrier();
             const u32x4 o = transposed_v<KV>(reinterpret_cast<const uint8_t*>(stage[w]), lane);
             __builtin_amdgcn_wave_barrier();
             const int j0 = (hc0 - h * nchunk);
-            char* vreg = static_cast<char*>(a.v_cache) + (tile * d + (size_t)j0 * X) * kBlock * kCacheBytes;
-            *reinterpret_cast<u32x4*>(vreg + 16 * lane) = o;
+            const int off0 = s0 & (bs - 1);   // the unit's first token in the block
+            const size_t vrow = tile * d + (size_t)j0 * X + lane / kCacheBytes;
+            char* vdst = static_cast<char*>(a.v_cache) + (vrow * bs + off0) * kCacheBytes +
+                         16 * (lane % kCacheBytes);
+            *reinterpret_cast<u32x4*>(vdst) = o;
         } else if (live) {
             // V: dims j*X .. j*X+X-1 of the tile, one element per dim row at `off`
             char* vdst = static_cast<char*>(a.v_cache) +
-                         ((tile * d + (size_t)j * X) * kBlock + off) * kCacheBytes;
+                         ((tile * d + (size_t)j * X) * bs + off) * kCacheBytes;
 #pragma unroll
             for (int e = 0; e < X; ++e) {
                 if constexpr (KV == KV_FP8)
-                    reinterpret_cast<uint8_t*>(vdst)[e * kBlock] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
+                    reinterpret_cast<uint8_t*>(vdst)[e * bs] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
                 else if constexpr (KV == KV_BF16)
-                    reinterpret_cast<uint16_t*>(vdst)[e * kBlock] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+                    reinterpret_cast<uint16_t*>(vdst)[e * bs] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
                 else
-                    reinterpret_cast<unsigned*>(vdst)[e * kBlock] = vw[e];
+                    reinterpret_cast<unsigned*>(vdst)[e * bs] = vw[e];
             }
         }
     }

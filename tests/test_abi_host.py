@@ -72,7 +72,7 @@ def decode_call(**over):
     (dict(max_len=4097), SHAPE),                      # beyond max_blocks * block_size
     (dict(part=-16), SHAPE), (dict(scale=float("nan")), SHAPE), (dict(scale=0.0), SHAPE),
     (dict(scale=-0.1), SHAPE),
-    (dict(d=96), UNSUP), (dict(bs=32), UNSUP), (dict(hq=136), UNSUP),   # G = 17
+    (dict(d=96), UNSUP), (dict(bs=48), UNSUP), (dict(bs=128), UNSUP), (dict(hq=136), UNSUP),
     (dict(part=24), UNSUP),
     (dict(q=P + 8), ALIGN), (dict(k=P + 4), ALIGN), (dict(out=P + 2), ALIGN),
     (dict(bt=P + 2), ALIGN),
@@ -143,7 +143,7 @@ def write_call(**over):
     (dict(ind=2), DTYPE),                     # fp8 is not an input type
     (dict(ind=7, kv=7), DTYPE),
     (dict(d=96), UNSUP),
-    (dict(bs=32), UNSUP),
+    (dict(bs=48), UNSUP),
     (dict(T=-1), SHAPE),
     (dict(kst=1023), SHAPE),                  # stride shorter than a token's row
     (dict(kst=1028), ALIGN),                  # row start not 16-byte aligned
