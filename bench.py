@@ -236,6 +236,24 @@ def time_verify(torch, pa, W, steps, warmup, flush, partition_size):
     return res
 
 
+def time_block_sizes(torch, pa, W, steps, warmup, flush):
+    """The headline batch (C2's lengths, heads and data recipe) paged with
+    32- and 64-token blocks, balanced split-KV."""
+    from workloads.device import Dev
+    res = {}
+    for bs in (32, 64):
+        w = W.decode_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              len_lo=512, len_hi=4096, q_dtype="bf16", kv_dtype="bf16",
+                              block_size=bs, pad=0, name=f"C2 bs={bs}")
+        d = Dev(w)
+        s, _ = time_decode(torch, pa, d, w, -1, steps, warmup, flush)
+        ms = sum(s) / len(s)
+        res[str(bs)] = {"ms_per_step": round(ms, 5), "kv_GBps": round(w.kv_bytes() / ms / 1e6, 2),
+                        "pct_hbm_peak": round(100 * w.kv_bytes() / ms / 1e6 / HBM_PEAK_GBS, 2)}
+        del d
+    return res
+
+
 def write_cases(W):
     """Cache writes of the decode and prefill steps above, and a long-context
     fill: (label, WriteWorkload, pool blocks).  The caches are allocated on
@@ -341,6 +359,9 @@ def profile_one(args, W):
         return
     if args.partition_size < 0 and args.workload in ("C4", "C5"):
         args.partition_size = 1024   # the per-config default of these workloads
+    if args.workload == "BLOCKS":
+        print(json.dumps(time_block_sizes(torch, pa, W, args.steps, args.warmup, flush)), flush=True)
+        return
     if args.workload == "WRITE":
         for wl in write_cases(W):
             print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
@@ -375,10 +396,10 @@ def main():
                          "balanced split (equal work per resident workgroup), 0 = one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY"],
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY", "BLOCKS"],
                     help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
                          "plus the others under per_config; WRITE = the cache writes, VERIFY = draft "
-                         "verification)")
+                         "verification, BLOCKS = 32/64-token blocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -452,6 +473,7 @@ def main():
         del dd, dp
         per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
         per_config["verify"] = time_verify(torch, pa, W, 20, 3, flush, args.partition_size)
+        per_config["block_size"] = time_block_sizes(torch, pa, W, 20, 3, flush)
 
     kv = head["kv_GBps"]
     line = {
