@@ -192,6 +192,36 @@ int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len,
                      void* workspace, size_t workspace_bytes, int stages, void* stream);
 
 /*
+ * Decode with a shared prefix (cascade): every sequence's cache is the same
+ * prefix_len-token prefix (whole blocks, listed once in prefix_block_table)
+ * followed by its own tokens (block_table / seq_lens describe only those:
+ * seq_lens[b] tokens after the prefix, the current token(s) included).  The
+ * result equals pa_decode_multi_query over the concatenated sequence (prefix
+ * caching shares such blocks: vllm-metis 0.1.0, "How the model maps onto
+ * vLLM"), but the prefix is read once for the whole batch instead of once per
+ * sequence: (1) all queries against the prefix, split into key ranges, give
+ * partial results; (2) each sequence's own tokens, split into partitions of
+ * partition_size (> 0) tokens; (3) the log-sum-exp merge of both.
+ * q, out [num_seqs, q_len, num_q_heads, head_dim] (q_len * G <= 16; q_len 1
+ * is plain decode); workspace of at least
+ * pa_decode_shared_prefix_workspace_size(...) bytes.  prefix_len 0 is
+ * pa_decode_multi_query in one pass.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int q_len, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int prefix_len,
+                                              int max_seq_len, int partition_size);
+
+int pa_decode_shared_prefix(void* out, const void* q, int q_dtype, int q_len,
+                            const void* k_cache, const void* v_cache, int kv_dtype,
+                            const int32_t* prefix_block_table, int prefix_len,
+                            const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int num_seqs,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, const float* k_scale,
+                            const float* v_scale, int partition_size, int max_seq_len,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-KV decode, partition kernel only: writes partial_out / partial_lse
  * for every partition of every sequence (partitions past ceil(L / P) are not
  * written and must not be read; pa_merge_partitions ignores them).

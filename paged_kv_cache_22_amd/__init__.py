@@ -12,12 +12,12 @@ Importing the package loads ``libpa.so`` and fails if it is not built
 (``python paged_kv_cache_22_amd/build.py``).
 """
 from ._binding import (LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALANCED, PAError, decode,
-                       decode_multi_query, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
+                       decode_multi_query, decode_shared_prefix, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
                        PA_STAGE_ALL,
                        decode_partitions, decode_workspace_size, lib, merge_partitions,
                        prefill_chunk, status_string, write_kv)
 
-__all__ = ["decode", "decode_multi_query", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
+__all__ = ["decode", "decode_multi_query", "decode_shared_prefix", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
            "PA_STAGE_ALL", "decode_partitions", "merge_partitions", "prefill_chunk", "write_kv",
            "decode_workspace_size", "status_string", "PAError", "lib", "LIB_PATH",
            "PA_F32", "PA_BF16", "PA_FP8_E4M3", "PA_PARTITION_BALANCED"]

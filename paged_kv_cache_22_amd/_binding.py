@@ -31,6 +31,9 @@ SIGNATURES = {
                                    _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "pa_decode_stages": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
                               _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _i, _vp]),
+    "pa_decode_shared_prefix_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "pa_decode_shared_prefix": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _vp, _i, _i,
+                                     _i, _i, _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i,
                                   _i, _i, _i, _f, _vp, _vp, _i, _i, _vp]),
     "pa_merge_partitions": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
@@ -203,6 +206,39 @@ def decode_stages(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: in
                               int(partition_size), int(max_seq_len), _dev(workspace, "workspace"),
                               ws_bytes, int(stages), _stream(q))
     _check("pa_decode_stages", st)
+    return out
+
+
+def decode_shared_prefix(q, k_cache, v_cache, prefix_block_table, prefix_len: int, block_table,
+                         seq_lens, *, max_seq_len: int, partition_size: int = 1024,
+                         scale: Optional[float] = None, k_scale=None, v_scale=None, out=None,
+                         workspace=None):
+    """Cascade decode over a shared prefix (pa_decode_shared_prefix).  q is
+    [B, Hq, d] or [B, q_len, Hq, d]; block_table / seq_lens cover each
+    sequence's tokens after the prefix."""
+    torch = _torch()
+    qn = q.shape[1] if q.dim() == 4 else 1
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+    _, _, _, NB, Hkv, bs = _kv_dims(q.reshape(B, qn * Hq, d), k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = d ** -0.5
+    need = int(lib.pa_decode_shared_prefix_workspace_size(B, qn, Hq, Hkv, d, int(prefix_len),
+                                                          int(max_seq_len), int(partition_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_shared_prefix(_dev(out, "out"), _dev(q, "q"), _dtype_code(q, False), qn,
+                                     _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                     _dtype_code(k_cache, True),
+                                     _dev(prefix_block_table, "prefix_block_table"), int(prefix_len),
+                                     _dev(block_table, "block_table"), block_table.shape[1],
+                                     _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d, bs, NB, float(scale),
+                                     _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                                     int(partition_size), int(max_seq_len),
+                                     _dev(workspace, "workspace"), ws_bytes, _stream(q))
+    _check("pa_decode_shared_prefix", st)
     return out
 
 

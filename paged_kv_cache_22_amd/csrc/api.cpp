@@ -104,6 +104,28 @@ pa::DecodeArgs make_decode_args(const void* q, int q_dtype, const void* k_cache,
 
 int hip_status(int e) { return e == 0 ? PA_OK : PA_ERR_HIP; }
 
+// Key ranges of the shared-prefix pass: enough (row group, kv-head, range)
+// workgroups to cover the chip (kPrefixWGs), each range at least 32 tokens
+constexpr int kPrefixWGs = 512;
+
+// tokens per key range (a multiple of 32): about kPrefixWGs / (row groups x
+// kv-heads) ranges over the prefix
+int prefix_key_range(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int prefix_len) {
+    const long long rows = (long long)num_seqs * q_len * (num_q_heads / num_kv_heads);
+    const long long groups = (rows + 127) / 128 * num_kv_heads;   // 128 rows per workgroup
+    long long want = (kPrefixWGs + groups - 1) / groups;
+    if (want < 1) want = 1;
+    const long long per = (prefix_len + want - 1) / want;
+    return (int)((per + 31) / 32 * 32);
+}
+
+// the ranges that key range actually makes (every one holds keys)
+int prefix_ranges(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int prefix_len) {
+    if (prefix_len <= 0) return 0;
+    const int kr = prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
+    return (prefix_len + kr - 1) / kr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +413,122 @@ int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len, const voi
                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        block_size, scale, k_scale, v_scale, partition_size, max_seq_len, workspace,
                        workspace_bytes, stream, stages);
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int q_len, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int prefix_len,
+                                              int max_seq_len, int partition_size) {
+    if (num_seqs < 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        prefix_len < 0 || max_seq_len < 0 || partition_size <= 0)
+        return 0;
+    const size_t slots = (size_t)prefix_ranges(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len) +
+                         ((size_t)max_seq_len + partition_size - 1) / partition_size;
+    const size_t rows = (size_t)num_seqs * q_len * num_q_heads * slots;
+    return round_up(rows * head_dim * sizeof(float), kRegionAlign) +
+           round_up(rows * sizeof(float), kRegionAlign);
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
+                            const void* v_cache, int kv_dtype, const int32_t* prefix_block_table,
+                            int prefix_len, const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            float scale, const float* k_scale, const float* v_scale,
+                            int partition_size, int max_seq_len, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (q_len <= 0 || prefix_len < 0) return PA_ERR_SHAPE;
+    if (partition_size <= 0) return PA_ERR_UNSUPPORTED;
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (prefix_len % block_size != 0) return PA_ERR_UNSUPPORTED;  // the prefix is whole blocks
+    if (prefix_len > 0 && num_seqs > 0 && !prefix_block_table) return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(prefix_block_table) & 3u) return PA_ERR_ALIGN;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    const int G = num_q_heads / num_kv_heads;
+    if ((long long)q_len * G > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * q_len * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const size_t need = pa_decode_shared_prefix_workspace_size(
+        num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, prefix_len, max_seq_len, partition_size);
+    if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kRegionAlign - 1))) return PA_ERR_ALIGN;
+    if (num_seqs == 0) return PA_OK;
+    if (prefix_len == 0)
+        return decode_impl(out, q, q_dtype, q_len, k_cache, v_cache, kv_dtype, block_table,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                           head_dim, block_size, scale, k_scale, v_scale, 0, max_seq_len, nullptr, 0,
+                           stream);
+
+    const int ranges = prefix_ranges(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
+    const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
+    const int slots = ranges + parts;
+    const size_t rows = (size_t)num_seqs * q_len * num_q_heads;
+    char* ws = reinterpret_cast<char*>(workspace);
+    float* part_out = reinterpret_cast<float*>(ws);
+    float* part_lse = reinterpret_cast<float*>(ws + round_up(rows * slots * head_dim * sizeof(float), kRegionAlign));
+
+    // 1. every query of the batch against the shared prefix, split into key ranges
+    pa::PrefillArgs p{};
+    p.q = q;
+    p.q_dtype = q_dtype;
+    p.uniform_q_len = num_seqs * q_len;     // one chunk: all queries, in (sequence, query) order
+    p.total_q = num_seqs * q_len;
+    p.max_q_len = num_seqs * q_len;
+    p.num_chunks = 1;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.kv_dtype = kv_dtype;
+    p.block_table = prefix_block_table;
+    p.max_blocks_per_seq = prefix_len / block_size;
+    p.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    p.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.scale = scale;
+    p.kv_len = prefix_len;
+    p.key_range = prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
+    p.part_out = part_out;
+    p.part_lse = part_lse;
+    p.part_stride = slots;
+    st = hip_status(pa::launch_prefill(p, stream));
+    if (st != PA_OK) return st;
+
+    // 2. each sequence's own tokens, split-KV partitions in the slots after the ranges
+    pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
+                                        max_blocks_per_seq, seq_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, block_size, scale, k_scale, v_scale);
+    a.q_len = q_len;
+    if (parts > 0) {
+        a.part_out = part_out;
+        a.part_lse = part_lse;
+        a.single_direct = 0;
+        a.part_offset = ranges;
+        a.max_parts = slots;
+        a.partition_blocks = partition_size / kUnit;
+        a.grid_parts = parts;
+        st = hip_status(pa::launch_decode(a, stream));
+        if (st != PA_OK) return st;
+    }
+
+    // 3. the log-sum-exp merge of prefix ranges and suffix partitions
+    pa::MergeArgs m{};
+    m.out = out;
+    m.out_dtype = q_dtype;
+    m.part_out = part_out;
+    m.part_lse = part_lse;
+    m.seq_lens = seq_lens;
+    m.partition_size = partition_size;
+    m.max_parts = slots;
+    m.lead_slots = ranges;
+    m.num_seqs = num_seqs;
+    m.num_q_heads = q_len * num_q_heads;
+    m.head_dim = head_dim;
+    m.skip_single = 0;
+    return hip_status(pa::launch_merge(m, stream));
 }
 
 int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, const int32_t* cu_q_lens,

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     const int np = (nblk + pb - 1) / pb;
     RangeOut dst;
     dst.direct = !SPLIT || (np == 1 && a.single_direct);
-    dst.prow_base = (size_t)part;
+    dst.prow_base = (size_t)(part + a.part_offset);
     dst.prow_stride = (size_t)a.max_parts;
     attend_range<D, KIND, BS, MQ, WAVES>(a, b, h, L, j0, j1, dst, smem);
 }

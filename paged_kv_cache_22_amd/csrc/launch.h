@@ -14,6 +14,7 @@ struct DecodeArgs {
     float* part_lse;      // [B, Hq, max_parts]
     int single_direct;    // split mode: a sequence with one partition writes `out`
                           // directly instead of a partial (the merge then skips it)
+    int part_offset;      // split mode: partition p goes to partial slot p + part_offset
     int max_parts;
     const void* q;
     const void* k_cache;
@@ -45,6 +46,8 @@ struct MergeArgs {
     int partition_size, max_parts;
     int num_seqs, num_q_heads, head_dim;
     int skip_single;      // leave sequences with exactly one partition untouched
+    int lead_slots;       // partition mode: partials 0 .. lead_slots-1 precede the
+                          // sequence's partitions (a shared prefix's key ranges)
     // balanced split-KV pieces (instead of partition_size / max_parts):
     // partial row of (kv-head h, slot, column) = (h * piece_slots + slot) * cols + column
     const void* piece_info;  // int2 [num_seqs] = (first slot, count); NULL: partition mode
@@ -69,6 +72,15 @@ struct PrefillArgs {
     int num_chunks, num_q_heads, num_kv_heads, head_dim;
     int block_size;       // tokens per cache block: 16, 32 or 64
     int uniform_q_len;    // > 0: chunk c owns rows c*uniform_q_len .. (cu_q_lens unused)
+    // key-range mode (kv_len > 0): every row of chunk c sees keys
+    // [z * key_range, min((z + 1) * key_range, kv_len)) of its table row,
+    // z = blockIdx.z, with no causal mask (seq_lens unused)
+    int kv_len, key_range;
+    // partial output (part_out non-NULL): fp32 normalised rows and lse at
+    // partial index row * part_stride + (kv_len > 0 ? z : 0), instead of out
+    float* part_out;
+    float* part_lse;
+    int part_stride;
     int max_blocks_per_seq;
     float scale;
 };

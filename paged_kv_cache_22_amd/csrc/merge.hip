@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         base = ((size_t)h * a.piece_slots + info.x) * cols + col;
         pstride = cols;
     } else {
-        np = min((L + a.partition_size - 1) / a.partition_size, a.max_parts);
+        np = a.lead_slots + min((L + a.partition_size - 1) / a.partition_size,
+                                a.max_parts - a.lead_slots);
         base = row * a.max_parts;
         pstride = 1;
     }

@@ -54,12 +54,17 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const int ch = blockIdx.x / Hkv;
     const int qbeg = a.uniform_q_len > 0 ? ch * a.uniform_q_len : a.cu_q_lens[ch];
     const int qlen = a.uniform_q_len > 0 ? a.uniform_q_len : a.cu_q_lens[ch + 1] - qbeg;
-    const int L = a.seq_lens[ch];
+    // key-range mode: keys [ubeg * 16, kend) of a kv_len-token sequence, all
+    // visible to every row; otherwise causal keys 0 .. ctx + i
+    const bool ranged = a.kv_len > 0;
+    const int L = ranged ? a.kv_len : a.seq_lens[ch];
     const int ctx = L - qlen;
+    const int ubeg = ranged ? (int)blockIdx.z * (a.key_range / kBS) : 0;
+    const int kend = ranged ? min(L, ((int)blockIdx.z + 1) * a.key_range) : L;
     const int nrho = qlen * G;
     const int rho_wg = blockIdx.y * (16 * NC * kWaves);
     if (rho_wg >= nrho) return;  // uniform
-    if (ctx < 0) {
+    if (!ranged && ctx < 0) {
         // fewer cached tokens than queries (an idle sequence has none): the
         // rows see no keys; they get zeros and lse -inf, and nothing is read
 #pragma unroll
@@ -76,13 +81,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         return;
     }
 
-    // key blocks the workgroup needs, and this wave's share of the rows
-    const int nblk = (ctx + (min(nrho, rho_wg + 16 * NC * kWaves) - 1) / G) / kBS + 1;
+    // the last key query i sees
+    auto qpos = [&](int i) { return ranged ? kend - 1 : ctx + i; };
+    // key units the workgroup needs (up to nblk), and this wave's share of the rows
+    const int nblk = qpos((min(nrho, rho_wg + 16 * NC * kWaves) - 1) / G) / kBS + 1;
     const int rho0 = rho_wg + w * 16 * NC;
     const bool wave_rows = rho0 < nrho;
     const int w_last = min(nrho, rho0 + 16 * NC) - 1;
-    const int w_nblk = wave_rows ? (ctx + w_last / G) / kBS + 1 : 0;   // blocks this wave sees
-    const int full_end = wave_rows ? (ctx + rho0 / G + 1) / kBS : 0;   // no mask below this
+    const int w_nblk = wave_rows ? qpos(w_last / G) / kBS + 1 : 0;     // units this wave sees
+    const int full_end = wave_rows ? (qpos(rho0 / G) + 1) / kBS : 0;   // no mask below this
 
     int pos[NC];
     bool ok[NC];
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         const int rho = rho0 + 16 * ct + r;
         ok[ct] = rho < nrho;
         const int i = rho / G, g = rho - (rho / G) * G;
-        pos[ct] = ok[ct] ? ctx + i : ctx + w_last / G;
+        pos[ct] = ok[ct] ? qpos(i) : qpos(w_last / G);
         qrow_idx[ct] = (qbeg + i) * Hq + h * G + g;
         T::load_q(Q[ct], ok[ct] ? reinterpret_cast<const QT*>(a.q) + (size_t)qrow_idx[ct] * D : nullptr, c);
     }
@@ -103,8 +110,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     // block-table window (every wave holds the same 64 entries): lane i holds
     // the table entry of unit tbase + i, unit u lying in block u / (BS / 16)
     const int32_t* trow = a.block_table + (size_t)ch * a.max_blocks_per_seq;
-    int tbase = 0;
-    int tcur = (lane < nblk) ? trow[lane >> kSubShift] : 0;
+    int tbase = ubeg;
+    int tcur = (ubeg + lane < nblk) ? trow[(ubeg + lane) >> kSubShift] : 0;
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
     const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
@@ -174,8 +181,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         T::load_lds(RB, stage[buf][1], stage[buf][1] + TB, r, c);
         const int jB = jA + 1;
         const bool needB = jB < w_nblk;
-        const int validA = L - jA * kBS;
-        const int validB = needB ? L - jB * kBS : 0;
+        const int validA = kend - jA * kBS;
+        const int validB = needB ? kend - jB * kBS : 0;
         if (validA < kBS) T::mask_v(RA, c, validA);  // cache slots past L
         if (validB < kBS) T::mask_v(RB, c, validB);
         const bool diag = jB >= full_end || !needB;
@@ -210,12 +217,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         }
     };
 
-    const int nsteps = (nblk + kStepBlocks - 1) / kStepBlocks;
-    fetch(0);
+    const int nsteps = (nblk - ubeg + kStepBlocks - 1) / kStepBlocks;
+    fetch(ubeg);
     stash(0);
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
-        const int j0 = s * kStepBlocks;
+        const int j0 = ubeg + s * kStepBlocks;
         if (s + 1 < nsteps) {
             if (j0 + 2 * kStepBlocks - 1 - tbase >= 64) {  // next step leaves the table window
                 tbase += 64 - kStepBlocks;                  // keep the 2 steps in one window
@@ -234,6 +241,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         l[ct] = group_sum4(l[ct]);
         if (!ok[ct]) continue;
         const float inv = vscale / l[ct];
+        if (a.part_out) {
+            const size_t pidx = (size_t)qrow_idx[ct] * a.part_stride + (ranged ? blockIdx.z : 0);
+            float* po = a.part_out + pidx * D;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                store4(po + 16 * n + 4 * c, acc[ct][n][0] * inv, acc[ct][n][1] * inv,
+                       acc[ct][n][2] * inv, acc[ct][n][3] * inv);
+            if (c == 0) a.part_lse[pidx] = (m[ct] * C + fast_log2(l[ct])) * kLn2;
+            continue;
+        }
         QT* o = reinterpret_cast<QT*>(a.out) + (size_t)qrow_idx[ct] * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
@@ -253,7 +270,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const long rows = (long)a.max_q_len * G;
     const long per_wg = 16L * kNC * kWaves;
-    dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + per_wg - 1) / per_wg));
+    const unsigned ranges = a.kv_len > 0 ? (unsigned)((a.kv_len + a.key_range - 1) / a.key_range) : 1u;
+    dim3 grid((unsigned)(a.num_chunks * a.num_kv_heads), (unsigned)((rows + per_wg - 1) / per_wg), ranges);
     hipLaunchKernelGGL((prefill_kernel<D, KIND, BS, kNC>), grid, dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }

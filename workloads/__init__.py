@@ -51,6 +51,7 @@ __all__ = [
     "config1", "config2", "config3", "config4", "config5", "build_config",
     "decode_workload", "prefill_workload", "to_bf16_bits", "to_fp8_codes",
     "WriteWorkload", "write_workload", "write_chunks", "write_decode_step",
+    "SharedPrefixWorkload", "shared_prefix_workload",
     "kv_bytes_per_token", "CONFIG_NAMES",
 ]
 
@@ -537,3 +538,60 @@ def write_decode_step(*, seed: int, num_seqs: int, num_blocks: int,
         raise ValueError("pool too small for the sequences")
     offs = rng.integers(0, block_size, num_seqs)
     return (blocks * block_size + offs).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# decode batches whose sequences share a cached prefix
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class SharedPrefixWorkload:
+    """Decode sequences that all start with the same prefix_len cached tokens
+    (the same physical blocks), each followed by its own tokens.  ``full`` is
+    the plain view (whole block tables, whole lengths); the prefix table and
+    the suffix tables / lengths are the cascade's view of the same cache."""
+    full: DecodeWorkload
+    prefix_len: int
+    prefix_table: np.ndarray      # int32 [1, prefix_len / block_size]
+    suffix_table: np.ndarray      # int32 [B, max suffix blocks]
+    suffix_lens: np.ndarray       # int32 [B]
+
+
+def shared_prefix_workload(*, seed: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, prefix_len: int, len_lo: int, len_hi: int,
+                           q_dtype: str, kv_dtype: str, q_len: int = 0,
+                           block_size: int = BLOCK_SIZE, suffix_lens=None,
+                           name: str = "shared prefix") -> SharedPrefixWorkload:
+    """Suffix lengths uniform integers in [len_lo, len_hi] (after the
+    prefix_len-token prefix, a multiple of block_size).  Pool order: the
+    prefix's blocks, then each sequence's own blocks, all from one
+    permutation; K/V/q drawn as for decode_workload."""
+    if prefix_len % block_size:
+        raise ValueError("the prefix must be whole blocks")
+    rng = np.random.default_rng(seed)
+    if suffix_lens is None:
+        suffix_lens = rng.integers(len_lo, len_hi, size=num_seqs, endpoint=True)
+    sfx = np.asarray(suffix_lens, dtype=np.int32)
+    npre = prefix_len // block_size
+    nsfx = [-(-int(L) // block_size) for L in sfx]
+    nb = max(npre + sum(nsfx), 1)
+    perm = rng.permutation(nb).astype(np.int32)
+    prefix_table = perm[:npre].reshape(1, npre) if npre else np.zeros((1, 1), np.int32)
+    max_sfx = max(max(nsfx, default=0), 1)
+    suffix_table = np.full((num_seqs, max_sfx), -1, dtype=np.int32)
+    full_table = np.full((num_seqs, npre + max_sfx), -1, dtype=np.int32)
+    pos = npre
+    for b, n in enumerate(nsfx):
+        suffix_table[b, :n] = perm[pos:pos + n]
+        full_table[b, :npre] = perm[:npre]
+        full_table[b, npre:npre + n] = perm[pos:pos + n]
+        pos += n
+    qshape = (num_seqs, num_q_heads, head_dim) if q_len == 0 else \
+        (num_seqs, q_len, num_q_heads, head_dim)
+    q = _draw_q(rng, qshape, q_dtype)
+    k, v, ks, vs = _make_pools(seed, nb, num_kv_heads, head_dim, block_size, kv_dtype)
+    full = DecodeWorkload(name=name, q=q, k_cache=k, v_cache=v, block_table=full_table,
+                          seq_lens=(sfx + prefix_len).astype(np.int32), q_dtype=q_dtype,
+                          kv_dtype=kv_dtype, scale=1.0 / math.sqrt(head_dim), k_scale=ks,
+                          v_scale=vs)
+    return SharedPrefixWorkload(full=full, prefix_len=prefix_len, prefix_table=prefix_table,
+                                suffix_table=suffix_table, suffix_lens=sfx)
