@@ -254,6 +254,64 @@ def time_block_sizes(torch, pa, W, steps, warmup, flush):
     return res
 
 
+def time_shared_prefix(torch, pa, W, steps, warmup, flush):
+    """64 sequences (32/8 heads, d=128, bf16) sharing a 2048-token prefix,
+    each with U[512, 4096] tokens of its own (seed 2): pa_decode (balanced)
+    over the whole tables, which reads the prefix once per sequence, against
+    pa_decode_shared_prefix, which reads it once for the batch."""
+    import numpy as np
+    from workloads.device import dev
+    sp = W.shared_prefix_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8,
+                                  head_dim=128, prefix_len=2048, len_lo=512, len_hi=4096,
+                                  q_dtype="bf16", kv_dtype="bf16", name="shared prefix")
+    wl = sp.full
+    q, k, v = dev(wl.q, "bf16"), dev(wl.k_cache, "bf16"), dev(wl.v_cache, "bf16")
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    pt, st, sfl = dev(sp.prefix_table), dev(sp.suffix_table), dev(sp.suffix_lens)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                                  wl.max_seq_len, -1), 256),
+                     dtype=torch.uint8, device="cuda")
+    smax = int(sp.suffix_lens.max())
+    ws2 = torch.empty(max(int(pa.lib.pa_decode_shared_prefix_workspace_size(
+        wl.num_seqs, 1, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2048, smax, 1024)), 256),
+        dtype=torch.uint8, device="cuda")
+
+    def plain(ev):
+        ev[0].record()
+        pa.decode(q, k, v, bt, sl, max_seq_len=wl.max_seq_len, scale=wl.scale, partition_size=-1,
+                  out=out, workspace=ws)
+        ev[1].record()
+
+    def cascade(ev):
+        ev[0].record()
+        pa.decode_shared_prefix(q, k, v, pt, 2048, st, sfl, max_seq_len=smax, partition_size=1024,
+                                scale=wl.scale, out=out, workspace=ws2)
+        ev[1].record()
+
+    unique = 2048 * 8 * 128 * 2 * 2 + int(sp.suffix_lens.astype(np.int64).sum()) * 8 * 128 * 2 * 2
+    res = {"workload": "64 seqs sharing a 2048-token prefix + U[512,4096] own tokens, seed 2, "
+                       "32/8 heads, d=128, bf16",
+           "kv_bytes_attended": wl.kv_bytes(), "kv_bytes_unique": unique}
+    for name, fn in (("plain_balanced", plain), ("cascade", cascade)):
+        wt = Timer(torch, warmup, 2)
+        for i in range(warmup):
+            flush()
+            fn(wt.ev[i])
+        torch.cuda.synchronize()
+        t = Timer(torch, steps, 2)
+        for i in range(steps):
+            flush()
+            fn(t.ev[i])
+        torch.cuda.synchronize()
+        ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
+        res[name] = {"ms": round(ms, 5),
+                     "tokens_attended_per_s": round(wl.total_tokens / ms * 1e3, 1),
+                     "attended_kv_GBps": round(wl.kv_bytes() / ms / 1e6, 2),
+                     "unique_kv_GBps": round(unique / ms / 1e6, 2)}
+    return res
+
+
 def write_cases(W):
     """Cache writes of the decode and prefill steps above, and a long-context
     fill: (label, WriteWorkload, pool blocks).  The caches are allocated on
@@ -359,6 +417,9 @@ def profile_one(args, W):
         return
     if args.partition_size < 0 and args.workload in ("C4", "C5"):
         args.partition_size = 1024   # the per-config default of these workloads
+    if args.workload == "PREFIX":
+        print(json.dumps(time_shared_prefix(torch, pa, W, args.steps, args.warmup, flush)), flush=True)
+        return
     if args.workload == "BLOCKS":
         print(json.dumps(time_block_sizes(torch, pa, W, args.steps, args.warmup, flush)), flush=True)
         return
@@ -396,10 +457,10 @@ def main():
                          "balanced split (equal work per resident workgroup), 0 = one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY", "BLOCKS"],
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY", "BLOCKS", "PREFIX"],
                     help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
                          "plus the others under per_config; WRITE = the cache writes, VERIFY = draft "
-                         "verification, BLOCKS = 32/64-token blocks)")
+                         "verification, BLOCKS = 32/64-token blocks, PREFIX = a shared-prefix batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -474,6 +535,7 @@ def main():
         per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
         per_config["verify"] = time_verify(torch, pa, W, 20, 3, flush, args.partition_size)
         per_config["block_size"] = time_block_sizes(torch, pa, W, 20, 3, flush)
+        per_config["shared_prefix"] = time_shared_prefix(torch, pa, W, 20, 3, flush)
 
     kv = head["kv_GBps"]
     line = {
