@@ -561,7 +561,7 @@ def main():
         "tokens_attended_per_s": head["tokens_attended_per_s"],
         "timing": {"p10_ms": head["p10_ms"], "p50_ms": head["p50_ms"], "p90_ms": head["p90_ms"],
                    "wall_s_incl_cache_flush": round(wall, 3),
-                   "note": "per-step HIP events around the launches; a 1 GiB rewrite before "
+                   "note": "per-step HIP events around the launches; a 1 GiB read before "
                            "each step evicts the Infinity Cache and is not timed"},
         "roofline": {
             "kernel": ("decode_balanced_kernel<128, bf16>" if args.partition_size < 0 else

@@ -61,7 +61,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         jobs.append([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, f), "-o", obj])
         objs.append(obj)
     api_obj = os.path.join(BUILD, "api.cpp.o")
-    jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c",
+    host_defs = [f for f in extra_flags if f.startswith("-D")]
+    jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", *host_defs, "-c",
                  os.path.join(CSRC, "api.cpp"), "-o", api_obj])
     objs.append(api_obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:

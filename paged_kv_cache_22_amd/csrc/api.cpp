@@ -106,7 +106,10 @@ int hip_status(int e) { return e == 0 ? PA_OK : PA_ERR_HIP; }
 
 // Key ranges of the shared-prefix pass: enough (row group, kv-head, range)
 // workgroups to cover the chip (kPrefixWGs), each range at least 32 tokens
-constexpr int kPrefixWGs = 512;
+#ifndef PA_PREFIX_WGS
+#define PA_PREFIX_WGS 256
+#endif
+constexpr int kPrefixWGs = PA_PREFIX_WGS;
 
 // tokens per key range (a multiple of 32): about kPrefixWGs / (row groups x
 // kv-heads) ranges over the prefix
