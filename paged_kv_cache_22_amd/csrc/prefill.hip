@@ -125,7 +125,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             const int p = tid + u * 64 * kWaves;
             const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
             const int jb = min(j0 + (tile >> 1), nblk - 1);  // a missing 2nd block re-reads the 1st
-            const int phys = __shfl(tcur, jb - tbase, 64);
+            // tile (hence jb) is uniform over the wave: the table entry comes
+            // from one lane into a scalar register
+            const int phys = __builtin_amdgcn_readlane(tcur, __builtin_amdgcn_readfirstlane(jb - tbase));
             const int sub = jb & ((1 << kSubShift) - 1);    // unit within the block
             // the piece's place in the block's tile: K chunk runs and V rows
             // are BS tokens long, the unit's 16 tokens at offset 16 * sub
@@ -160,12 +162,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         }
     };
 
-    float m[NC], l[NC];
+    // m: running max (raw score units); accl: the weights' column sums,
+    // accumulated by MFMA (every element of a lane's accl holds its column's sum)
+    float m[NC];
+    f32x4 accl[NC];
     f32x4 acc[NC][NT];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
         m[ct] = -INFINITY;
-        l[ct] = 0.f;
+        accl[ct] = zero4();
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[ct][n] = zero4();
     }
@@ -204,16 +209,22 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             const float mn = fmaxf(m[ct], bm);
             if (__ballot((mn - m[ct]) * C > kRescaleLog2)) {
                 const float alpha = fast_exp2((m[ct] - mn) * C);
-                l[ct] *= alpha;
+                accl[ct] *= alpha;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
                 m[ct] = mn;
             }
+            // exp2(t * C - m * C) as one FMA per weight: at the maximum it
+            // leaves the rounding error of m * C, far below bf16's resolution,
+            // so the packed weight is exactly 1 there and the normaliser (the
+            // sum of the packed weights) matches it
+            const float mc = m[ct] * C;
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2((t[e] - m[ct]) * C);
-            l[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            T::pv2(RA, RB, p, acc[ct]);
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[e], C, -mc));
+            const auto pk = T::pack_p2(p);
+            T::pv2(RA, RB, pk, acc[ct]);
+            T::lsum2(pk, accl[ct]);
         }
     };
 
@@ -238,9 +249,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
-        l[ct] = group_sum4(l[ct]);
+        const float lsum = accl[ct][0];
         if (!ok[ct]) continue;
-        const float inv = vscale / l[ct];
+        const float inv = vscale / lsum;
         if (a.part_out) {
             const size_t pidx = (size_t)qrow_idx[ct] * a.part_stride + (ranged ? blockIdx.z : 0);
             float* po = a.part_out + pidx * D;
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             for (int n = 0; n < NT; ++n)
                 store4(po + 16 * n + 4 * c, acc[ct][n][0] * inv, acc[ct][n][1] * inv,
                        acc[ct][n][2] * inv, acc[ct][n][3] * inv);
-            if (c == 0) a.part_lse[pidx] = (m[ct] * C + fast_log2(l[ct])) * kLn2;
+            if (c == 0) a.part_lse[pidx] = (m[ct] * C + fast_log2(lsum)) * kLn2;
             continue;
         }
         QT* o = reinterpret_cast<QT*>(a.out) + (size_t)qrow_idx[ct] * D;
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         for (int n = 0; n < NT; ++n)
             store4(o + 16 * n + 4 * c, acc[ct][n][0] * inv, acc[ct][n][1] * inv,
                    acc[ct][n][2] * inv, acc[ct][n][3] * inv);
-        if (a.out_lse && c == 0) a.out_lse[qrow_idx[ct]] = (m[ct] * C + fast_log2(l[ct])) * kLn2;
+        if (a.out_lse && c == 0) a.out_lse[qrow_idx[ct]] = (m[ct] * C + fast_log2(lsum)) * kLn2;
     }
 }
 

@@ -83,12 +83,21 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
     // two blocks in one K=32 product: k-slots (c, 0..3) are block A's tokens
     // 4c..4c+3 and (c, 4..7) block B's, matching p[0..3] / p[4..7]
-    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
-        const u32x4 pb{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    using P2 = u32x4;   // the 8 weights as the bf16 B operand
+    __device__ static P2 pack_p2(const float p[8]) {
+        return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    }
+    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pb, f32x4* acc) {
 #pragma unroll
         for (int n = 0; n < NT; ++n)
             acc[n] = mfma_16x16x32_bf16(u32x4{A.v[n].x, A.v[n].y, B.v[n].x, B.v[n].y}, pb, acc[n]);
+    }
+    // column sums of the (bf16) weights, the normaliser that matches pv2
+    // exactly: an all-ones A operand, every D row holds the sum
+    __device__ static void lsum2(const P2& pb, f32x4& accl) {
+        constexpr unsigned kOnes = 0x3f803f80u;   // two bf16 1.0
+        accl = mfma_16x16x32_bf16(u32x4{kOnes, kOnes, kOnes, kOnes}, pb, accl);
     }
 };
 
@@ -149,14 +158,21 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(fp8x4_to_bf16x4(R.v[n]), pb, acc[n]);
     }
-    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
-        const u32x4 pb{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    using P2 = u32x4;
+    __device__ static P2 pack_p2(const float p[8]) {
+        return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    }
+    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pb, f32x4* acc) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const u32x2 a = fp8x4_to_bf16x4(A.v[n]), b = fp8x4_to_bf16x4(B.v[n]);
             acc[n] = mfma_16x16x32_bf16(u32x4{a.x, a.y, b.x, b.y}, pb, acc[n]);
         }
+    }
+    __device__ static void lsum2(const P2& pb, f32x4& accl) {
+        constexpr unsigned kOnes = 0x3f803f80u;
+        accl = mfma_16x16x32_bf16(u32x4{kOnes, kOnes, kOnes, kOnes}, pb, accl);
     }
 };
 
@@ -212,9 +228,21 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
             for (int e = 0; e < 4; ++e)
                 acc[n] = mfma_16x16x4_f32(__uint_as_float(R.v[n][e]), p[e], acc[n]);
     }
-    __device__ static void pv2(const Regs& A, const Regs& B, const float p[8], f32x4* acc) {
-        pv(A, p, acc);
-        pv(B, p + 4, acc);
+    struct P2 { float p[8]; };
+    __device__ static P2 pack_p2(const float p[8]) {
+        P2 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.p[e] = p[e];
+        return r;
+    }
+    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pk, f32x4* acc) {
+        pv(A, pk.p, acc);
+        pv(B, pk.p + 4, acc);
+    }
+    // column sums by MFMA with a ones operand, as for the other kinds
+    __device__ static void lsum2(const P2& pk, f32x4& accl) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accl = mfma_16x16x4_f32(1.0f, pk.p[e], accl);
     }
 };
 

@@ -66,7 +66,7 @@ def test_prefill_ragged(bs, kv):
                                         wl.k_scale, wl.v_scale)
     got, lse = run_prefill(Dev(wl), want_lse=True)
     compare(f64(got), ref, kv, f"prefill bs={bs} {kv}")
-    assert np.abs(f64(lse) - ref_lse).max() < 1e-3
+    assert np.abs(f64(lse) - ref_lse).max() < (1e-3 if kv == "f32" else 2e-3)  # bf16 weights: ln(1 + 2^-9)
 
 
 @pytest.mark.parametrize("bs", BS)

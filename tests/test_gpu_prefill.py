@@ -17,6 +17,12 @@ def oracle_prefill(wl, items=None):
                                 wl.v_scale, items=items)
 
 
+# The normaliser is the sum of the weights as they enter the PV product
+# (bf16 for bf16 / fp8 KV), so the lse carries their rounding:
+# |error| <= ln(1 + 2^-9) ~ 1.95e-3.  fp32 weights stay fp32.
+LSE_TOL = {"f32": 1e-3, "bf16": 2e-3, "fp8": 2e-3}
+
+
 def rows_mask(ref):
     return ~np.isnan(ref[..., 0])
 
@@ -32,7 +38,7 @@ def test_ragged_chunks(kv, d_head):
     ref, ref_lse = oracle_prefill(wl)
     got, lse = run_prefill(d, want_lse=True)
     compare(f64(got), ref, kv, f"prefill ragged {kv} d={d_head}")
-    assert np.abs(f64(lse) - ref_lse).max() < 1e-3
+    assert np.abs(f64(lse) - ref_lse).max() < LSE_TOL[kv]
 
 
 def test_empty_chunks():
