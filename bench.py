@@ -469,8 +469,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the kernels run on one GPU's share; see DESIGN.md for how it would shard)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernels "
+              f"run on one GPU's share of the batch; the multi-GPU split is not built)",
               file=sys.stderr)
         sys.exit(2)
 
