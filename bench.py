@@ -19,7 +19,7 @@ fp8 KV, the cache writes that precede attention, and draft verification with
 several queries per sequence) are timed the same way and reported under
 "per_config".  The
 CPU-baseline leg times the fp64 oracle on the host over the whole headline
-batch (single thread).
+batch, repeated for at least 10 s (single thread).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
@@ -68,20 +68,29 @@ def stored_traffic(partition_size):
     return int(kv["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands, single-threaded, over the whole batch."""
+def cpu_baseline(wl, min_seconds=10.0):
+    """The oracle as it stands, single-threaded: the whole batch, repeated
+    until at least min_seconds of CPU work, the mean pass reported."""
     import oracle
     from threadpoolctl import threadpool_limits
+    passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
-                      wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
-        dt = time.perf_counter() - t0
+        while True:
+            oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                          wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
+            passes += 1
+            total = time.perf_counter() - t0
+            if total >= min_seconds:
+                break
+    dt = total / passes
     return {"value": round(wl.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": passes,
+            "seconds": round(total, 2),
             "tokens_attended_per_s": round(wl.total_tokens / dt, 1),
-            "sample": f"whole batch: {wl.num_seqs} sequences, {wl.total_tokens} tokens, "
-                      f"all {wl.num_kv_heads} kv-heads (fp64 numpy oracle, 1 thread)"}
+            "sample": f"the whole batch ({wl.num_seqs} sequences, {wl.total_tokens} tokens, "
+                      f"all {wl.num_kv_heads} kv-heads), {passes} passes, fp64 numpy oracle, "
+                      f"1 thread"}
 
 
 class CacheFlush:
