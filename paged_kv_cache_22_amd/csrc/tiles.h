@@ -54,7 +54,10 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
     // the same lane layout read from a tile staged in LDS (plain loads)
     // V rows in LDS are kVRowLds bytes apart (padded: conflict-free reads)
-    static constexpr int kVRow = kBS * 2, kVRowLds = kVRow + 8;
+#ifndef PA_VROW_LDS_BF16
+#define PA_VROW_LDS_BF16 (kBS * 2 + 8)
+#endif
+    static constexpr int kVRow = kBS * 2, kVRowLds = PA_VROW_LDS_BF16;
     __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
