@@ -424,8 +424,8 @@ def profile_one(args, W):
         print(json.dumps(time_verify(torch, pa, W, args.steps, args.warmup, flush,
                                      args.partition_size)), flush=True)
         return
-    if args.partition_size < 0 and args.workload in ("C4", "C5"):
-        args.partition_size = 1024   # the per-config default of these workloads
+    if args.partition_size < 0 and args.workload == "C5":
+        args.partition_size = 1024   # its best: short sequences of similar length
     if args.workload == "PREFIX":
         print(json.dumps(time_shared_prefix(torch, pa, W, args.steps, args.warmup, flush)), flush=True)
         return
@@ -439,7 +439,7 @@ def profile_one(args, W):
     n = int(args.workload[1])
     res = {"workload": W.CONFIG_NAMES[n]}
     if n == 4:
-        m = W.config4(pad=0, partition_size=1024)
+        m = W.config4(pad=0, partition_size=args.partition_size)
         dd, dp = Dev(m.decode), Dev(m.prefill)
         s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, args.steps,
                            args.warmup, flush)
@@ -524,12 +524,14 @@ def main():
             per_config[w.name]["balanced"] = {kk: vv for kk, vv in decode_summary(w, s, k).items()
                                               if kk in ("ms_per_step", "kv_GBps", "pct_hbm_peak")}
             del dd
-        m = W.config4(pad=0, partition_size=1024)
+        # the mixed step's decode rows (16 long sequences) balanced across the chip
+        m = W.config4(pad=0, partition_size=-1)
         dd, dp = Dev(m.decode), Dev(m.prefill)
         s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, 20, 3, flush)
         pms = time_prefill(torch, pa, dp, m.prefill, 20, 3, flush)
         pre_ms = sum(pms) / len(pms)
         dec = decode_summary(m.decode, s, k)
+        dec["partition_size"] = m.decode.partition_size
         tflops = m.prefill.flops() / pre_ms / 1e9
         per_config["C4"] = {
             "workload": W.CONFIG_NAMES[4],
