@@ -121,6 +121,20 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 acc) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// a wave-uniform global pointer pinned to scalar registers: adding a lane's
+// 32-bit offset to it then selects the scalar-base form of the global load,
+// and the compiler cannot fold the lane part into a per-lane 64-bit address
+typedef const char __attribute__((address_space(1))) gchar;
+__device__ __forceinline__ gchar* uniform_ptr(const char* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ u32x4 ld16(gchar* p) {
+    return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
+}
+
 // 16-byte / 8-byte / 4-byte global loads (plain vector loads)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

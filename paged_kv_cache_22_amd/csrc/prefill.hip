@@ -10,16 +10,19 @@
 // Layout of the work.  The chunk's (query, head-of-group) pairs are numbered
 // rho = i * G + g and cut into 16-wide MFMA column tiles.  A workgroup of 4
 // waves owns 4 * NC tiles of one (chunk, kv-head); each wave owns NC tiles.
-// Key blocks go two at a time through a double-buffered LDS stage: the
-// workgroup loads a step's K and V tiles once, every thread one or more
-// contiguous 16-byte pieces (plain loads, so blocks that several chunks share
-// -- a common prefix -- can be served by L2), while the previous step is
-// computed; one barrier per step.  K tiles keep their HBM layout in LDS and V
-// rows are padded by 8 bytes, so each wave reads its MFMA operands the way
-// decode reads them from HBM, without LDS bank conflicts.  Per block and
-// column tile: S^T = K . Q^T on MFMA, online softmax per column (base 2),
-// then O^T += V^T . P^T.  Blocks wholly below a wave's diagonal skip the
-// mask; row sums stay per lane until the end.
+// Key units go two at a time through a double-buffered LDS stage: the
+// workgroup loads a step's K and V units once, every lane contiguous 16-byte
+// pieces (plain loads, so blocks that several chunks share -- a common
+// prefix -- can be served by L2), while the previous step is computed; one
+// barrier per step.  Each of a wave's loads lies in one unit tile, so the
+// block-table lookup and the tile's base address are scalar and only the
+// lane's (loop-invariant) offset is a vector register.  K units keep their
+// HBM layout in LDS; the two V units share one region whose rows interleave
+// them by groups of 4 tokens, so a lane reads the whole K=32 operand of the
+// output product in one piece.  Per step and column tile: S^T = K . Q^T on
+// MFMA, online softmax per column (base 2), then O^T += V^T . P^T; the
+// weights' column sums go through the MFMA too.  Steps wholly below a wave's
+// diagonal skip the mask.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -38,12 +41,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
     constexpr int TB = T::kUnitBytes;                       // one 16-token K (or V) unit
     constexpr int kUnitRun = kBS * 16;                       // one K chunk run of a unit
-    constexpr int kVLds = D * T::kVRowLds;                   // one V tile in LDS (padded rows)
-    constexpr int kSlot = (TB + kVLds + 15) / 16 * 16;       // K then V of one block
-    constexpr int kPieces = kStepBlocks * 2 * TB / 16;       // 16-byte pieces per step
+    constexpr int kTilePieces = TB / 16;                     // 16-byte pieces per unit
+    static_assert(kTilePieces % 64 == 0, "a wave's load lies in one unit");
+    constexpr int kPieces = kStepBlocks * 2 * kTilePieces;   // per step: 2 units of K and V
     constexpr int kPerThread = kPieces / (64 * kWaves);
     static_assert(kPieces % (64 * kWaves) == 0, "every thread loads whole pieces");
-    __shared__ __attribute__((aligned(16))) char stage[2][kStepBlocks][kSlot];
+    constexpr int kOffV = kStepBlocks * TB;                  // the V pair region
+    constexpr int kStage = (kOffV + D * T::kVPairRow + 15) / 16 * 16;
+    __shared__ __attribute__((aligned(16))) char stage[2][kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,48 +121,58 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
     const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
 
-    // global -> registers for one step: piece p is byte 16 * (p % (TB/16)) of
-    // tile p / (TB/16) = (block of the step, K or V)
+    // A step's pieces: wave w's load u covers pieces 64 * (w + 4u) + lane,
+    // which lie in one unit tile (uniform over the wave): tile = 2 * unit of
+    // the step + (0 for K, 1 for V).  off is the piece's byte in the unit's
+    // own layout; voff its place in the cache block's tile (K chunk runs and
+    // V rows are BS tokens long there), both fixed for the whole loop.
+    auto piece_tile = [&](int u) { return (64 * (w + kWaves * u)) / kTilePieces; };
+    auto piece_off = [&](int u) { return ((64 * (w + kWaves * u)) % kTilePieces + lane) * 16; };
+    int voff[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int off = piece_off(u);
+        voff[u] = (piece_tile(u) & 1)
+            ? (off / T::kVRow) * T::kVRow * (BS / kBS) + off % T::kVRow
+            : (off / kUnitRun) * kUnitRun * (BS / kBS) + off % kUnitRun;
+    }
+
+    // global -> registers for the step starting at unit j0 (a missing second
+    // unit re-reads the first, which the consumer masks)
     u32x4 held[kPerThread];
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < kPerThread; ++u) {
-            const int p = tid + u * 64 * kWaves;
-            const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
-            const int jb = min(j0 + (tile >> 1), nblk - 1);  // a missing 2nd block re-reads the 1st
-            // tile (hence jb) is uniform over the wave: the table entry comes
-            // from one lane into a scalar register
+            const int tile = piece_tile(u);
+            const int jb = min(j0 + (tile >> 1), nblk - 1);
             const int phys = __builtin_amdgcn_readlane(tcur, __builtin_amdgcn_readfirstlane(jb - tbase));
             const int sub = jb & ((1 << kSubShift) - 1);    // unit within the block
-            // the piece's place in the block's tile: K chunk runs and V rows
-            // are BS tokens long, the unit's 16 tokens at offset 16 * sub
-            const int goff = (tile & 1)
-                ? (off / T::kVRow) * T::kVRow * (BS / kBS) + sub * T::kUnitV + off % T::kVRow
-                : (off / kUnitRun) * kUnitRun * (BS / kBS) + sub * T::kUnitK + off % kUnitRun;
-            const char* src = ((tile & 1) ? vbase : kbase) + (size_t)phys * blk_stride + goff;
-            held[u] = ld16(src);
+            gchar* base = uniform_ptr((tile & 1)
+                ? vbase + (size_t)phys * blk_stride + sub * T::kUnitV
+                : kbase + (size_t)phys * blk_stride + sub * T::kUnitK);
+            held[u] = ld16(base + (uint32_t)voff[u]);
         }
     };
-    // registers -> LDS: K tiles verbatim, V rows re-strided to T::kVRowLds
+    // registers -> LDS: K units verbatim; V pieces split into their groups of
+    // 4 tokens, each to its place in the pair region
     auto stash = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < kPerThread; ++u) {
-            const int p = tid + u * 64 * kWaves;
-            const int tile = p / (TB / 16), off = (p % (TB / 16)) * 16;
-            char* slot = stage[buf][tile >> 1];
+            const int tile = piece_tile(u), off = piece_off(u), unit = tile >> 1;
             if (!(tile & 1)) {
-                *reinterpret_cast<u32x4*>(slot + off) = held[u];
+                *reinterpret_cast<u32x4*>(stage[buf] + unit * TB + off) = held[u];
+                continue;
+            }
+            const int row = off / T::kVRow, g0 = (off % T::kVRow) / T::kVGrp;
+            char* dst = stage[buf] + kOffV + row * T::kVPairRow + unit * T::kVGrp + g0 * 2 * T::kVGrp;
+            if constexpr (T::kVGrp == 16) {
+                *reinterpret_cast<u32x4*>(dst) = held[u];
+            } else if constexpr (T::kVGrp == 8) {
+                reinterpret_cast<u32x2*>(dst)[0] = u32x2{held[u].x, held[u].y};
+                reinterpret_cast<u32x2*>(dst + 16)[0] = u32x2{held[u].z, held[u].w};
             } else {
-                char* dst = slot + TB + (off / T::kVRow) * T::kVRowLds + off % T::kVRow;
-                if constexpr (T::kVRowLds % 16 == 0) {
-                    *reinterpret_cast<u32x4*>(dst) = held[u];
-                } else if constexpr (T::kVRowLds % 8 == 0) {
-                    reinterpret_cast<u32x2*>(dst)[0] = u32x2{held[u].x, held[u].y};
-                    reinterpret_cast<u32x2*>(dst)[1] = u32x2{held[u].z, held[u].w};
-                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) reinterpret_cast<unsigned*>(dst)[e] = held[u][e];
-                }
+                for (int e = 0; e < 4; ++e) reinterpret_cast<unsigned*>(dst + 8 * e)[0] = held[u][e];
             }
         }
     };
@@ -175,21 +190,22 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         for (int n = 0; n < NT; ++n) acc[ct][n] = zero4();
     }
 
-    // The two blocks of a step (jA, jA+1) against every column tile of this
+    // The two units of a step (jA, jA+1) against every column tile of this
     // wave: 8 scores per lane, one online-softmax round over 32 keys, one
-    // K=32 MFMA per output tile.  A block the wave does not need (past its
+    // K=32 MFMA per output tile.  A unit the wave does not need (past its
     // diagonal, or past the sequence) has all its scores masked to -inf and
     // its V zeroed, so it adds exactly nothing.
     auto consume2 = [&](int buf, int jA) {
-        typename T::Regs RA, RB;
-        T::load_lds(RA, stage[buf][0], stage[buf][0] + TB, r, c);
-        T::load_lds(RB, stage[buf][1], stage[buf][1] + TB, r, c);
+        typename T::KRegs RA, RB;
+        typename T::VPair VP;
+        T::load_k_lds(RA, stage[buf], r, c);
+        T::load_k_lds(RB, stage[buf] + TB, r, c);
+        T::load_vpair(VP, stage[buf] + kOffV, r, c);
         const int jB = jA + 1;
         const bool needB = jB < w_nblk;
         const int validA = kend - jA * kBS;
         const int validB = needB ? kend - jB * kBS : 0;
-        if (validA < kBS) T::mask_v(RA, c, validA);  // cache slots past L
-        if (validB < kBS) T::mask_v(RB, c, validB);
+        if (validA < kBS || validB < kBS) T::mask_vpair(VP, c, validA, validB);  // slots past L
         const bool diag = jB >= full_end || !needB;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[e], C, -mc));
             const auto pk = T::pack_p2(p);
-            T::pv2(RA, RB, pk, acc[ct]);
+            T::pv2(VP, pk, acc[ct]);
             T::lsum2(pk, accl[ct]);
         }
     };

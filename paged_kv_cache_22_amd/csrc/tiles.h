@@ -28,6 +28,17 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 //         start; BS: the block's token count, the K chunk and V row stride)
 //   qk    S^T fragment: lane (r, c) gets scores of head r, tokens 4c..4c+3
 //   pv    acc[n] += V^T[16n..16n+15, tokens] . P^T for this block
+// and for prefill, which stages two 16-token units (A, B) of K and V in LDS
+// and contracts over both in one K=32 product:
+//   KRegs / load_k_lds   one unit's K operand read from its LDS copy (the
+//                        HBM layout, kept verbatim)
+//   VPair / load_vpair   both units' V operand from the pair region: in
+//                        dim row d, lane group c owns kVGrp bytes of unit A
+//                        (tokens 4c..4c+3) followed by the same of unit B,
+//                        so a lane reads its k-slots (c, 0..7) in one piece;
+//                        rows are kVPairRow bytes apart (padded: the 16
+//                        rows one read instruction touches hit distinct banks)
+//   pv2   acc[n] += V^T . P^T over the 32 tokens; lsum2 the weights' sums
 // ---------------------------------------------------------------------------
 template <int KIND, int D, int BS = kBS> struct Tile;
 
@@ -52,19 +63,33 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (BS * 2) + c * 8);
     }
-    // the same lane layout read from a tile staged in LDS (plain loads)
-    // V rows in LDS are kVRowLds bytes apart (padded: conflict-free reads)
-#ifndef PA_VROW_LDS_BF16
-#define PA_VROW_LDS_BF16 (kBS * 2 + 8)
-#endif
-    static constexpr int kVRow = kBS * 2, kVRowLds = PA_VROW_LDS_BF16;
-    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+    struct KRegs { u32x4 k[KL]; };
+    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld8(vt + (16 * n + r) * kVRowLds + c * 8);
     }
-    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+    static constexpr int kVRow = kBS * 2, kVGrp = 8;   // a unit's V row; 4 tokens
+#ifndef PA_VPAIR_ROW_BF16
+#define PA_VPAIR_ROW_BF16 80
+#endif
+    static constexpr int kVPairRow = PA_VPAIR_ROW_BF16;
+    struct VPair { u32x4 v[NT]; };
+    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) P.v[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 16);
+    }
+    // zero the V of tokens at or past va (unit A) / vb (unit B)
+    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
+        const int t0 = 4 * c;
+        const u32x4 mk = {(t0 + 0 < va ? 0x0000ffffu : 0u) | (t0 + 1 < va ? 0xffff0000u : 0u),
+                          (t0 + 2 < va ? 0x0000ffffu : 0u) | (t0 + 3 < va ? 0xffff0000u : 0u),
+                          (t0 + 0 < vb ? 0x0000ffffu : 0u) | (t0 + 1 < vb ? 0xffff0000u : 0u),
+                          (t0 + 2 < vb ? 0x0000ffffu : 0u) | (t0 + 3 < vb ? 0xffff0000u : 0u)};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) P.v[n] &= mk;
+    }
+    template <class KR>
+    __device__ static f32x4 qk(const KR& R, const QOp& Q) {
         f32x4 s = zero4();
 #pragma unroll
         for (int i = 0; i < KL; ++i) s = mfma_16x16x32_bf16(R.k[i], Q.b[i], s);
@@ -84,17 +109,16 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(R.v[n], pb, acc[n]);
     }
-    // two blocks in one K=32 product: k-slots (c, 0..3) are block A's tokens
-    // 4c..4c+3 and (c, 4..7) block B's, matching p[0..3] / p[4..7]
+    // two units in one K=32 product: k-slots (c, 0..3) are unit A's tokens
+    // 4c..4c+3 and (c, 4..7) unit B's, matching p[0..3] / p[4..7]
     using P2 = u32x4;   // the 8 weights as the bf16 B operand
     __device__ static P2 pack_p2(const float p[8]) {
         return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
-    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pb, f32x4* acc) {
+    __device__ static void pv2(const VPair& P, const P2& pb, f32x4* acc) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-            acc[n] = mfma_16x16x32_bf16(u32x4{A.v[n].x, A.v[n].y, B.v[n].x, B.v[n].y}, pb, acc[n]);
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x32_bf16(P.v[n], pb, acc[n]);
     }
     // column sums of the (bf16) weights, the normaliser that matches pv2
     // exactly: an all-ones A operand, every D row holds the sum
@@ -128,14 +152,30 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * BS + c * 4);
     }
-    static constexpr int kVRow = kBS, kVRowLds = kVRow + 4;
-    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+    struct KRegs { u32x4 k[KL]; };
+    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld4(vt + (16 * n + r) * kVRowLds + c * 4);
     }
-    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+    static constexpr int kVRow = kBS, kVGrp = 4, kVPairRow = 8 * kVGrp + 8;
+    struct VPair { u32x2 v[NT]; };   // .x unit A's 4 codes, .y unit B's
+    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) P.v[n] = ld8(vp + (16 * n + r) * kVPairRow + c * 8);
+    }
+    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
+        const int t0 = 4 * c;
+        unsigned ma = 0, mb = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ma |= (t0 + e < va ? 0xffu : 0u) << (8 * e);
+            mb |= (t0 + e < vb ? 0xffu : 0u) << (8 * e);
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) { P.v[n].x &= ma; P.v[n].y &= mb; }  // code 0x00 is +0
+    }
+    template <class KR>
+    __device__ static f32x4 qk(const KR& R, const QOp& Q) {
         f32x4 s = zero4();
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
@@ -166,10 +206,10 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
         return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
-    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pb, f32x4* acc) {
+    __device__ static void pv2(const VPair& P, const P2& pb, f32x4* acc) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            const u32x2 a = fp8x4_to_bf16x4(A.v[n]), b = fp8x4_to_bf16x4(B.v[n]);
+            const u32x2 a = fp8x4_to_bf16x4(P.v[n].x), b = fp8x4_to_bf16x4(P.v[n].y);
             acc[n] = mfma_16x16x32_bf16(u32x4{a.x, a.y, b.x, b.y}, pb, acc[n]);
         }
     }
@@ -200,14 +240,31 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (BS * 4) + c * 16);
     }
-    static constexpr int kVRow = kBS * 4, kVRowLds = kVRow + 16;
-    __device__ static void load_lds(Regs& R, const char* kt, const char* vt, int r, int c) {
+    struct KRegs { u32x4 k[KL]; };
+    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ld16(vt + (16 * n + r) * kVRowLds + c * 16);
     }
-    __device__ static f32x4 qk(const Regs& R, const QOp& Q) {
+    static constexpr int kVRow = kBS * 4, kVGrp = 16, kVPairRow = 8 * kVGrp + 16;
+    struct VPair { u32x4 a[NT], b[NT]; };
+    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            P.a[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 32);
+            P.b[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 32 + 16);
+        }
+    }
+    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                if (4 * c + e >= va) P.a[n][e] = 0u;
+                if (4 * c + e >= vb) P.b[n][e] = 0u;
+            }
+    }
+    template <class KR>
+    __device__ static f32x4 qk(const KR& R, const QOp& Q) {
         f32x4 s = zero4();
 #pragma unroll
         for (int i = 0; i < KL; ++i)
@@ -238,9 +295,14 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
         for (int e = 0; e < 8; ++e) r.p[e] = p[e];
         return r;
     }
-    __device__ static void pv2(const Regs& A, const Regs& B, const P2& pk, f32x4* acc) {
-        pv(A, pk.p, acc);
-        pv(B, pk.p + 4, acc);
+    __device__ static void pv2(const VPair& P, const P2& pk, f32x4* acc) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[n] = mfma_16x16x4_f32(__uint_as_float(P.a[n][e]), pk.p[e], acc[n]);
+                acc[n] = mfma_16x16x4_f32(__uint_as_float(P.b[n][e]), pk.p[4 + e], acc[n]);
+            }
     }
     // column sums by MFMA with a ones operand, as for the other kinds
     __device__ static void lsum2(const P2& pk, f32x4& accl) {
