@@ -126,6 +126,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
         // raw scores; the softmax scale (times log2 e, times the fp8 K scale)
         // is applied to differences from the running max, so the maximum's
         // weight is exactly exp2(0) = 1
+        T::settle(R);
         const f32x4 sc = T::qk(R, Q);
         float t[4] = {sc[0], sc[1], sc[2], sc[3]};
         const int valid = L - jj * kBS;

@@ -59,6 +59,27 @@ __device__ __forceinline__ float group_sum4(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// 4x4 transpose of 32-bit words over the four lane groups: on entry group c
+// holds x[0..3]; on exit slot j of group c holds what was x[c] of group j.
+// permlane32_swap exchanges the upper lane half of its first operand with the
+// lower half of its second, permlane16_swap the odd 16-lane rows of the first
+// with the even rows of the second: the first pass moves the off-diagonal
+// 2x2 word blocks between the halves, the second transposes each 2x2 block.
+__device__ __forceinline__ void group_transpose4(unsigned x[4]) {
+#pragma unroll
+    for (int jl = 0; jl < 2; ++jl) {
+        const auto p = __builtin_amdgcn_permlane32_swap(x[jl], x[2 + jl], false, false);
+        x[jl] = p[0];
+        x[2 + jl] = p[1];
+    }
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x[2 * jh], x[2 * jh + 1], false, false);
+        x[2 * jh] = p[0];
+        x[2 * jh + 1] = p[1];
+    }
+}
+
 // Reductions over the 16 lanes of one row (same c), by DPP-style xor shuffles.
 __device__ __forceinline__ float row_max16(float x) {
 #pragma unroll

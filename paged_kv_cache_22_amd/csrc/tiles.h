@@ -63,6 +63,7 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (BS * 2) + c * 8);
     }
+    __device__ static void settle(Regs&) {}   // loads land in MFMA layout
     struct KRegs { u32x4 k[KL]; };
     __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
 #pragma unroll
@@ -146,11 +147,24 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
                 Q.b[2 * i + hh] = qrow ? ld16(qrow + (4 * i + c) * 16 + 8 * hh)
                                        : u32x4{0u, 0u, 0u, 0u};
     }
+    // V: lane (r, c) reads the unit's whole 16-token row of dim 16(4m + c) + r
+    // as one 16-byte piece (word j = tokens 4j..4j+3); settle() then hands
+    // word c of dim 16n + r to lane (r, c) as v[n], the layout pv() takes
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv4(vt + (16 * n + r) * BS + c * 4);
+        for (int m = 0; m < NT / 4; ++m) {
+            const u32x4 w = ldkv16(vt + (16 * (4 * m + c) + r) * BS);
+            R.v[4 * m] = w.x;
+            R.v[4 * m + 1] = w.y;
+            R.v[4 * m + 2] = w.z;
+            R.v[4 * m + 3] = w.w;
+        }
+    }
+    __device__ static void settle(Regs& R) {
+#pragma unroll
+        for (int m = 0; m < NT / 4; ++m) group_transpose4(R.v + 4 * m);
     }
     struct KRegs { u32x4 k[KL]; };
     __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
@@ -240,6 +254,7 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (BS * 4) + c * 16);
     }
+    __device__ static void settle(Regs&) {}
     struct KRegs { u32x4 k[KL]; };
     __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
 #pragma unroll
