@@ -10,19 +10,18 @@
 // Layout of the work.  The chunk's (query, head-of-group) pairs are numbered
 // rho = i * G + g and cut into 16-wide MFMA column tiles.  A workgroup of 4
 // waves owns 4 * NC tiles of one (chunk, kv-head); each wave owns NC tiles.
-// Key units go two at a time through a double-buffered LDS stage: the
-// workgroup loads a step's K and V units once, every lane contiguous 16-byte
-// pieces (plain loads, so blocks that several chunks share -- a common
-// prefix -- can be served by L2), while the previous step is computed; one
-// barrier per step.  Each of a wave's loads lies in one unit tile, so the
-// block-table lookup and the tile's base address are scalar and only the
-// lane's (loop-invariant) offset is a vector register.  K units keep their
-// HBM layout in LDS; the two V units share one region whose rows interleave
-// them by groups of 4 tokens, so a lane reads the whole K=32 operand of the
-// output product in one piece.  Per step and column tile: S^T = K . Q^T on
-// MFMA, online softmax per column (base 2), then O^T += V^T . P^T; the
-// weights' column sums go through the MFMA too.  Steps wholly below a wave's
-// diagonal skip the mask.
+// Key units go two at a time (a step) through a ring of kStages LDS stages,
+// filled by direct global-to-LDS copies (global_load_lds_dwordx4: 16 bytes
+// per lane, no registers, no LDS stores) issued kStages - 1 steps ahead, so
+// blocks that several chunks share -- a common prefix -- are served by L2
+// while earlier steps are computed.  Each step: wait for this wave's copies
+// of the step, one barrier (then every wave's copies have landed, and every
+// wave is done with the stage the next copy overwrites), issue the copies of
+// a later step, compute.  Per step and column tile: S^T = K . Q^T on MFMA in
+// two products X and Y whose rows give each lane 8 consecutive tokens of one
+// unit, online softmax per column (base 2), then O^T += V^T . P^T with each
+// lane's V operand one 16-byte piece; the weights' column sums go through the
+// MFMA too.  Steps wholly below a wave's diagonal skip the mask.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -31,7 +30,40 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kStepBlocks = 2;  // key blocks per LDS stage (consumed as a pair)
+
+// LDS address (offset in the workgroup's LDS) of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct copy: every lane's 16 bytes at base + voff go to LDS address
+// m0 + 16 * lane (base and m0 wave-uniform; the compiler loads m0 for the
+// operand).  Written as asm so that the compiler neither reorders memory
+// accesses across it nor inserts load-counter waits for it: the kernel waits
+// for its copies itself (wait_copies), and any wait the compiler places for
+// its own loads can only be stricter.
+__device__ __forceinline__ void copy16_to_lds(const char* base, uint32_t voff, uint32_t m0) {
+    // (readfirstlane returns a signed int: each half goes through uint32_t so
+    // that widening never sign-extends the low word into the high one)
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t ub = ((uint64_t)hi << 32) | lo;
+    asm volatile("global_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(ub), "{m0}"(__builtin_amdgcn_readfirstlane(m0)) : "memory");
+}
+// wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// workgroup barrier that also orders memory accesses for the compiler; LDS
+// reads issued before it have returned
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int D, int KIND, int BS, int NC>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
@@ -39,16 +71,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
     constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
-    constexpr int TB = T::kUnitBytes;                       // one 16-token K (or V) unit
-    constexpr int kUnitRun = kBS * 16;                       // one K chunk run of a unit
-    constexpr int kTilePieces = TB / 16;                     // 16-byte pieces per unit
-    static_assert(kTilePieces % 64 == 0, "a wave's load lies in one unit");
-    constexpr int kPieces = kStepBlocks * 2 * kTilePieces;   // per step: 2 units of K and V
-    constexpr int kPerThread = kPieces / (64 * kWaves);
-    static_assert(kPieces % (64 * kWaves) == 0, "every thread loads whole pieces");
-    constexpr int kOffV = kStepBlocks * TB;                  // the V pair region
-    constexpr int kStage = (kOffV + D * T::kVPairRow + 15) / 16 * 16;
-    __shared__ __attribute__((aligned(16))) char stage[2][kStage];
+    constexpr int UB = T::kUnitBytes;                       // one 16-token K (or V) unit
+    constexpr int kCopies = UB / 1024;                       // 1 KiB copies per unit
+    static_assert(UB % 1024 == 0 && kCopies * 4 % kWaves == 0, "whole copies per wave");
+    constexpr int kPerWave = kCopies * 4 / kWaves;           // copies per wave and step
+    // a stage: K of unit A, kKPad bytes, K of unit B, V of unit A, V of unit B
+    constexpr int kOffKB = UB + T::kKPad, kOffVA = 2 * UB + T::kKPad, kOffVB = 3 * UB + T::kKPad;
+    constexpr int kStage = 4 * UB + T::kKPad;
+    constexpr int kStages = kStage * 3 <= 64 * 1024 ? 3 : 2;
+    static_assert(kStage * kStages <= 64 * 1024, "LDS ring fits 64 KiB");
+    __shared__ __attribute__((aligned(16))) char stage[kStages][kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,69 +143,54 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     }
     const float kscale = KIND == KV_FP8 ? a.k_scale[h] : 1.0f;
     const float C = a.scale * kLog2e * kscale;
+    // Q has arrived before the loop (a wait the compiler sees, so it places
+    // none of its own inside the loop, where it would also wait for copies)
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // block-table window (every wave holds the same 64 entries): lane i holds
-    // the table entry of unit tbase + i, unit u lying in block u / (BS / 16)
-    const int32_t* trow = a.block_table + (size_t)ch * a.max_blocks_per_seq;
-    int tbase = ubeg;
-    int tcur = (ubeg + lane < nblk) ? trow[(ubeg + lane) >> kSubShift] : 0;
+    // the table row, read-only for the whole kernel: through the constant
+    // address space its uniform entries are scalar loads, which wait on their
+    // own counter rather than behind the copies in flight
+    const __attribute__((address_space(4))) int32_t* trow =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
+        (size_t)ch * a.max_blocks_per_seq;
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
     const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
 
-    // A step's pieces: wave w's load u covers pieces 64 * (w + 4u) + lane,
-    // which lie in one unit tile (uniform over the wave): tile = 2 * unit of
-    // the step + (0 for K, 1 for V).  off is the piece's byte in the unit's
-    // own layout; voff its place in the cache block's tile (K chunk runs and
-    // V rows are BS tokens long there), both fixed for the whole loop.
-    auto piece_tile = [&](int u) { return (64 * (w + kWaves * u)) / kTilePieces; };
-    auto piece_off = [&](int u) { return ((64 * (w + kWaves * u)) % kTilePieces + lane) * 16; };
-    int voff[kPerThread];
+    // Copy k of this wave in a step is copy q = w + kWaves * k of the step's
+    // 4 * kCopies: region q / kCopies (K of A, K of B, V of A, V of B), its
+    // KiB q % kCopies.  voff: the lane's byte in the block tile (unit 0), as
+    // the region's layout in LDS asks (K verbatim, V by v_slot_hbm); fixed
+    // for the whole loop.
+    uint32_t voff[kPerWave];
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-        const int off = piece_off(u);
-        voff[u] = (piece_tile(u) & 1)
-            ? (off / T::kVRow) * T::kVRow * (BS / kBS) + off % T::kVRow
-            : (off / kUnitRun) * kUnitRun * (BS / kBS) + off % kUnitRun;
+    for (int k = 0; k < kPerWave; ++k) {
+        const int q = w + kWaves * k, reg = q / kCopies;
+        const int b = (q % kCopies) * 1024 + lane * 16;   // byte of the unit's LDS copy
+        voff[k] = reg < 2 ? (uint32_t)((b / (kBS * 16)) * (BS * 16) + b % (kBS * 16))
+                          : (uint32_t)T::v_slot_hbm(b / 16);
     }
-
-    // global -> registers for the step starting at unit j0 (a missing second
-    // unit re-reads the first, which the consumer masks)
-    u32x4 held[kPerThread];
-    auto fetch = [&](int j0) {
-#pragma unroll
-        for (int u = 0; u < kPerThread; ++u) {
-            const int tile = piece_tile(u);
-            const int jb = min(j0 + (tile >> 1), nblk - 1);
-            const int phys = __builtin_amdgcn_readlane(tcur, __builtin_amdgcn_readfirstlane(jb - tbase));
-            const int sub = jb & ((1 << kSubShift) - 1);    // unit within the block
-            gchar* base = uniform_ptr((tile & 1)
-                ? vbase + (size_t)phys * blk_stride + sub * T::kUnitV
-                : kbase + (size_t)phys * blk_stride + sub * T::kUnitK);
-            held[u] = ld16(base + (uint32_t)voff[u]);
-        }
+    const int nsteps = (nblk - ubeg + 1) / 2;
+    // the physical blocks of step t's units (a missing second unit re-reads
+    // the first, which the consumer masks); uniform, so scalar loads
+    auto phys_of = [&](int t, int& pa, int& pb) {
+        const int ja = ubeg + 2 * t, jb = min(ja + 1, nblk - 1);
+        pa = trow[ja >> kSubShift];
+        pb = trow[jb >> kSubShift];
     };
-    // registers -> LDS: K units verbatim; V pieces split into their groups of
-    // 4 tokens, each to its place in the pair region
-    auto stash = [&](int buf) {
+    auto copy_step = [&](int t, int pa, int pb) {
+        const int ja = ubeg + 2 * t, jb = min(ja + 1, nblk - 1);
+        char* st = stage[t % kStages];
 #pragma unroll
-        for (int u = 0; u < kPerThread; ++u) {
-            const int tile = piece_tile(u), off = piece_off(u), unit = tile >> 1;
-            if (!(tile & 1)) {
-                *reinterpret_cast<u32x4*>(stage[buf] + unit * TB + off) = held[u];
-                continue;
-            }
-            const int row = off / T::kVRow, g0 = (off % T::kVRow) / T::kVGrp;
-            char* dst = stage[buf] + kOffV + row * T::kVPairRow + unit * T::kVGrp + g0 * 2 * T::kVGrp;
-            if constexpr (T::kVGrp == 16) {
-                *reinterpret_cast<u32x4*>(dst) = held[u];
-            } else if constexpr (T::kVGrp == 8) {
-                reinterpret_cast<u32x2*>(dst)[0] = u32x2{held[u].x, held[u].y};
-                reinterpret_cast<u32x2*>(dst + 16)[0] = u32x2{held[u].z, held[u].w};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) reinterpret_cast<unsigned*>(dst + 8 * e)[0] = held[u][e];
-            }
+        for (int k = 0; k < kPerWave; ++k) {
+            const int q = w + kWaves * k, reg = q / kCopies;
+            const int j = (reg & 1) ? jb : ja;
+            const int sub = j & ((1 << kSubShift) - 1);
+            const char* base = (reg < 2 ? kbase + sub * T::kUnitK : vbase + sub * T::kUnitV) +
+                               (size_t)((reg & 1) ? pb : pa) * blk_stride;
+            const int dst = (reg == 0 ? 0 : reg == 1 ? kOffKB : reg == 2 ? kOffVA : kOffVB) +
+                            (q % kCopies) * 1024;
+            copy16_to_lds(base, voff[k], lds_addr(st + dst));
         }
     };
 
@@ -191,33 +208,34 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     }
 
     // The two units of a step (jA, jA+1) against every column tile of this
-    // wave: 8 scores per lane, one online-softmax round over 32 keys, one
-    // K=32 MFMA per output tile.  A unit the wave does not need (past its
-    // diagonal, or past the sequence) has all its scores masked to -inf and
-    // its V zeroed, so it adds exactly nothing.
-    auto consume2 = [&](int buf, int jA) {
-        typename T::KRegs RA, RB;
-        typename T::VPair VP;
-        T::load_k_lds(RA, stage[buf], r, c);
-        T::load_k_lds(RB, stage[buf] + TB, r, c);
-        T::load_vpair(VP, stage[buf] + kOffV, r, c);
+    // wave: 8 scores per lane (tokens 8(c & 1) .. +7 of unit c >> 1), one
+    // online-softmax round over 32 keys, one K=32 MFMA per output tile.  A
+    // unit the wave does not need (past its diagonal, or past the sequence)
+    // has all its scores masked to -inf and its V zeroed, so it adds exactly
+    // nothing.
+    auto consume = [&](int buf, int jA) {
+        const char* st = stage[buf];
+        typename T::KRegs X, Y;
+        load_k_xy<T>(X, Y, st, st + kOffKB, r, c);
+        typename T::VOp V;
+        T::load_v_xy(V, st + ((c >> 1) ? kOffVB : kOffVA), r, c);
         const int jB = jA + 1;
         const bool needB = jB < w_nblk;
         const int validA = kend - jA * kBS;
         const int validB = needB ? kend - jB * kBS : 0;
-        if (validA < kBS || validB < kBS) T::mask_vpair(VP, c, validA, validB);  // slots past L
+        if (validA < kBS || validB < kBS) T::mask_v_xy(V, c, (c >> 1) ? validB : validA);  // slots past L
         const bool diag = jB >= full_end || !needB;
+        const bool unit_ok = (c >> 1) == 0 || needB;
+        const int kp0 = (jA + (c >> 1)) * kBS + 8 * (c & 1);   // key position of this lane's t[0]
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            const f32x4 sa = T::qk(RA, Q[ct]);   // raw scores, as in decode
-            const f32x4 sb = T::qk(RB, Q[ct]);
-            float t[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+            const f32x4 sx = T::qk(X, Q[ct]);   // raw scores, as in decode
+            const f32x4 sy = T::qk(Y, Q[ct]);
+            float t[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
             if (diag) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (jA * kBS + 4 * c + e > pos[ct]) t[e] = -INFINITY;
-                    if (!needB || jB * kBS + 4 * c + e > pos[ct]) t[4 + e] = -INFINITY;
-                }
+                for (int e = 0; e < 8; ++e)
+                    if (!unit_ok || kp0 + e > pos[ct]) t[e] = -INFINITY;
             }
             float bm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
                              fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
@@ -239,27 +257,34 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[e], C, -mc));
             const auto pk = T::pack_p2(p);
-            T::pv2(VP, pk, acc[ct]);
+            T::pv_xy(V, pk, acc[ct]);
             T::lsum2(pk, accl[ct]);
         }
     };
 
-    const int nsteps = (nblk - ubeg + kStepBlocks - 1) / kStepBlocks;
-    fetch(ubeg);
-    stash(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int j0 = ubeg + s * kStepBlocks;
-        if (s + 1 < nsteps) {
-            if (j0 + 2 * kStepBlocks - 1 - tbase >= 64) {  // next step leaves the table window
-                tbase += 64 - kStepBlocks;                  // keep the 2 steps in one window
-                tcur = (tbase + lane < nblk) ? trow[(tbase + lane) >> kSubShift] : 0;
-            }
-            fetch(j0 + kStepBlocks);  // in flight during this step's compute
+    // prologue: steps 0 .. kStages-2 in flight
+    int pa = 0, pb = 0;
+    phys_of(0, pa, pb);
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) {
+        if (t < nsteps) {
+            copy_step(t, pa, pb);
+            if (t + 1 < nsteps) phys_of(t + 1, pa, pb);
         }
-        if (j0 < w_nblk) consume2(s & 1, j0);
-        if (s + 1 < nsteps) stash((s + 1) & 1);
-        __syncthreads();
+    }
+    for (int s = 0; s < nsteps; ++s) {
+        // this wave's copies of step s are done once at most the later
+        // steps' copies (issued before this point) are outstanding
+        if (kStages == 3 && s + 1 < nsteps) wait_copies<kPerWave>();
+        else wait_copies<0>();
+        barrier_lds();
+        const int t = s + kStages - 1;
+        if (t < nsteps) {
+            copy_step(t, pa, pb);     // overwrites the stage step s - 1 used
+            if (t + 1 < nsteps) phys_of(t + 1, pa, pb);
+        }
+        const int j0 = ubeg + 2 * s;
+        if (j0 < w_nblk) consume(s % kStages, j0);
     }
 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;

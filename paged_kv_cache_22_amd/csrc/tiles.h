@@ -29,16 +29,21 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 //   qk    S^T fragment: lane (r, c) gets scores of head r, tokens 4c..4c+3
 //   pv    acc[n] += V^T[16n..16n+15, tokens] . P^T for this block
 // and for prefill, which stages two 16-token units (A, B) of K and V in LDS
-// and contracts over both in one K=32 product:
-//   KRegs / load_k_lds   one unit's K operand read from its LDS copy (the
-//                        HBM layout, kept verbatim)
-//   VPair / load_vpair   both units' V operand from the pair region: in
-//                        dim row d, lane group c owns kVGrp bytes of unit A
-//                        (tokens 4c..4c+3) followed by the same of unit B,
-//                        so a lane reads its k-slots (c, 0..7) in one piece;
-//                        rows are kVPairRow bytes apart (padded: the 16
-//                        rows one read instruction touches hit distinct banks)
-//   pv2   acc[n] += V^T . P^T over the 32 tokens; lsum2 the weights' sums
+// and contracts over both in one K=32 product.  The score rows are ordered
+// so that lane group c holds 8 consecutive tokens of one unit: row 4c + e of
+// product X is token 8(c & 1) + e of unit c >> 1, and product Y the same
+// tokens + 4.  A lane's 8 weights then pair with one contiguous 8-token
+// piece of a V row, so the output product reads its operand in one piece:
+//   KRegs / load_k_xy    the K operands of X and Y from the staged units (K
+//                        keeps its HBM layout in LDS; unit B starts kKPad
+//                        bytes past unit A's end, so the 16 rows one read
+//                        touches hit distinct banks)
+//   v_slot_hbm           where the 16-byte piece of LDS slot s of a staged V
+//                        unit comes from in the block tile (the slot order
+//                        swizzles pieces across banks)
+//   VOp / load_v_xy      the lane's 8-token piece of dim rows 16n + r
+//   mask_v_xy            zero the V of tokens at or past `valid`
+//   pv_xy  acc[n] += V^T . P^T over the 32 tokens; lsum2 the weights' sums
 // ---------------------------------------------------------------------------
 template <int KIND, int D, int BS = kBS> struct Tile;
 
@@ -65,29 +70,26 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
     __device__ static void settle(Regs&) {}   // loads land in MFMA layout
     struct KRegs { u32x4 k[KL]; };
-    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
-#pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
+    static constexpr int kKPad = 64;
+    // V slot s = 2 * row + (h ^ ((row >> 3) & 1)) holds tokens 8h..8h+7 of dim row
+    __device__ static int v_slot_hbm(int slot) {
+        const int row = slot >> 1, h = (slot & 1) ^ ((row >> 3) & 1);
+        return row * (BS * 2) + h * 16;
     }
-    static constexpr int kVRow = kBS * 2, kVGrp = 8;   // a unit's V row; 4 tokens
-#ifndef PA_VPAIR_ROW_BF16
-#define PA_VPAIR_ROW_BF16 80
-#endif
-    static constexpr int kVPairRow = PA_VPAIR_ROW_BF16;
-    struct VPair { u32x4 v[NT]; };
-    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
+    struct VOp { u32x4 v[NT]; };
+    __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
+        const int sw = (c & 1) ^ ((r >> 3) & 1);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) P.v[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 16);
+        for (int n = 0; n < NT; ++n) V.v[n] = ld16(vu + (2 * (16 * n + r) + sw) * 16);
     }
-    // zero the V of tokens at or past va (unit A) / vb (unit B)
-    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
-        const int t0 = 4 * c;
-        const u32x4 mk = {(t0 + 0 < va ? 0x0000ffffu : 0u) | (t0 + 1 < va ? 0xffff0000u : 0u),
-                          (t0 + 2 < va ? 0x0000ffffu : 0u) | (t0 + 3 < va ? 0xffff0000u : 0u),
-                          (t0 + 0 < vb ? 0x0000ffffu : 0u) | (t0 + 1 < vb ? 0xffff0000u : 0u),
-                          (t0 + 2 < vb ? 0x0000ffffu : 0u) | (t0 + 3 < vb ? 0xffff0000u : 0u)};
+    __device__ static void mask_v_xy(VOp& V, int c, int valid) {
+        const int t0 = 8 * (c & 1);
+        u32x4 mk;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) P.v[n] &= mk;
+        for (int k = 0; k < 4; ++k)
+            mk[k] = (t0 + 2 * k < valid ? 0x0000ffffu : 0u) | (t0 + 2 * k + 1 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) V.v[n] &= mk;
     }
     template <class KR>
     __device__ static f32x4 qk(const KR& R, const QOp& Q) {
@@ -110,18 +112,18 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x16_bf16(R.v[n], pb, acc[n]);
     }
-    // two units in one K=32 product: k-slots (c, 0..3) are unit A's tokens
-    // 4c..4c+3 and (c, 4..7) unit B's, matching p[0..3] / p[4..7]
-    using P2 = u32x4;   // the 8 weights as the bf16 B operand
+    // the 8 weights of lane group c (tokens 8(c & 1) + e of unit c >> 1) as
+    // the bf16 B operand of the K=32 output product
+    using P2 = u32x4;
     __device__ static P2 pack_p2(const float p[8]) {
         return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
-    __device__ static void pv2(const VPair& P, const P2& pb, f32x4* acc) {
+    __device__ static void pv_xy(const VOp& V, const P2& pb, f32x4* acc) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x32_bf16(P.v[n], pb, acc[n]);
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_16x16x32_bf16(V.v[n], pb, acc[n]);
     }
-    // column sums of the (bf16) weights, the normaliser that matches pv2
+    // column sums of the (bf16) weights, the normaliser that matches pv_xy
     // exactly: an all-ones A operand, every D row holds the sum
     __device__ static void lsum2(const P2& pb, f32x4& accl) {
         constexpr unsigned kOnes = 0x3f803f80u;   // two bf16 1.0
@@ -167,26 +169,24 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
         for (int m = 0; m < NT / 4; ++m) group_transpose4(R.v + 4 * m);
     }
     struct KRegs { u32x4 k[KL]; };
-    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
+    static constexpr int kKPad = 64;
+    // V slot s is the unit's 16-token row of dim s (one 16-byte piece)
+    __device__ static int v_slot_hbm(int slot) { return slot * BS; }
+    struct VOp { u32x2 v[NT]; };   // codes of tokens 8(c & 1) .. +7
+    __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
+        for (int n = 0; n < NT; ++n) V.v[n] = ld8(vu + (16 * n + r) * 16 + 8 * (c & 1));
     }
-    static constexpr int kVRow = kBS, kVGrp = 4, kVPairRow = 8 * kVGrp + 8;
-    struct VPair { u32x2 v[NT]; };   // .x unit A's 4 codes, .y unit B's
-    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) P.v[n] = ld8(vp + (16 * n + r) * kVPairRow + c * 8);
-    }
-    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
-        const int t0 = 4 * c;
-        unsigned ma = 0, mb = 0;
+    __device__ static void mask_v_xy(VOp& V, int c, int valid) {
+        const int t0 = 8 * (c & 1);
+        unsigned lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            ma |= (t0 + e < va ? 0xffu : 0u) << (8 * e);
-            mb |= (t0 + e < vb ? 0xffu : 0u) << (8 * e);
+            lo |= (t0 + e < valid ? 0xffu : 0u) << (8 * e);
+            hi |= (t0 + 4 + e < valid ? 0xffu : 0u) << (8 * e);
         }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) { P.v[n].x &= ma; P.v[n].y &= mb; }  // code 0x00 is +0
+        for (int n = 0; n < NT; ++n) { V.v[n].x &= lo; V.v[n].y &= hi; }  // code 0x00 is +0
     }
     template <class KR>
     __device__ static f32x4 qk(const KR& R, const QOp& Q) {
@@ -220,10 +220,10 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
         return u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
-    __device__ static void pv2(const VPair& P, const P2& pb, f32x4* acc) {
+    __device__ static void pv_xy(const VOp& V, const P2& pb, f32x4* acc) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            const u32x2 a = fp8x4_to_bf16x4(P.v[n].x), b = fp8x4_to_bf16x4(P.v[n].y);
+            const u32x2 a = fp8x4_to_bf16x4(V.v[n].x), b = fp8x4_to_bf16x4(V.v[n].y);
             acc[n] = mfma_16x16x32_bf16(u32x4{a.x, a.y, b.x, b.y}, pb, acc[n]);
         }
     }
@@ -256,26 +256,25 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
     }
     __device__ static void settle(Regs&) {}
     struct KRegs { u32x4 k[KL]; };
-    __device__ static void load_k_lds(KRegs& R, const char* kt, int r, int c) {
-#pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ld16(kt + ((4 * i + c) * kBS + r) * 16);
-    }
-    static constexpr int kVRow = kBS * 4, kVGrp = 16, kVPairRow = 8 * kVGrp + 16;
-    struct VPair { u32x4 a[NT], b[NT]; };
-    __device__ static void load_vpair(VPair& P, const char* vp, int r, int c) {
+    static constexpr int kKPad = 0;    // (keeps two fp32 stages of d = 128 within 64 KiB)
+    // V slot s = 4 * row + j holds tokens 4j..4j+3 of dim row
+    __device__ static int v_slot_hbm(int slot) { return (slot >> 2) * (BS * 4) + (slot & 3) * 16; }
+    struct VOp { u32x4 a[NT], b[NT]; };   // tokens 8(c & 1) + 0..3 and + 4..7
+    __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            P.a[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 32);
-            P.b[n] = ld16(vp + (16 * n + r) * kVPairRow + c * 32 + 16);
+            V.a[n] = ld16(vu + (4 * (16 * n + r) + 2 * (c & 1)) * 16);
+            V.b[n] = ld16(vu + (4 * (16 * n + r) + 2 * (c & 1) + 1) * 16);
         }
     }
-    __device__ static void mask_vpair(VPair& P, int c, int va, int vb) {
+    __device__ static void mask_v_xy(VOp& V, int c, int valid) {
+        const int t0 = 8 * (c & 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                if (4 * c + e >= va) P.a[n][e] = 0u;
-                if (4 * c + e >= vb) P.b[n][e] = 0u;
+                if (t0 + e >= valid) V.a[n][e] = 0u;
+                if (t0 + 4 + e >= valid) V.b[n][e] = 0u;
             }
     }
     template <class KR>
@@ -310,13 +309,14 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
         for (int e = 0; e < 8; ++e) r.p[e] = p[e];
         return r;
     }
-    __device__ static void pv2(const VPair& P, const P2& pk, f32x4* acc) {
+    // output MFMA e (e = 0..7): k-slot c stands for token 8(c & 1) + e of unit c >> 1
+    __device__ static void pv_xy(const VOp& V, const P2& pk, f32x4* acc) {
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[n] = mfma_16x16x4_f32(__uint_as_float(P.a[n][e]), pk.p[e], acc[n]);
-                acc[n] = mfma_16x16x4_f32(__uint_as_float(P.b[n][e]), pk.p[4 + e], acc[n]);
+                acc[n] = mfma_16x16x4_f32(__uint_as_float(V.a[n][e]), pk.p[e], acc[n]);
+                acc[n] = mfma_16x16x4_f32(__uint_as_float(V.b[n][e]), pk.p[4 + e], acc[n]);
             }
     }
     // column sums by MFMA with a ones operand, as for the other kinds
@@ -325,6 +325,23 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
         for (int e = 0; e < 8; ++e) accl = mfma_16x16x4_f32(1.0f, pk.p[e], accl);
     }
 };
+
+// K operands of the score products X and Y from two staged units (kA, kB:
+// their LDS copies, in the HBM layout).  Row 4c + e of X is token
+// 8(c & 1) + e of unit c >> 1, row 4c + e of Y token 8(c & 1) + 4 + e: lane
+// (r, c) reads chunk 4i + c of token 8((r >> 2) & 1) + (r & 3) (+ 4 for Y)
+// of unit r >> 3.
+template <class T>
+__device__ __forceinline__ void load_k_xy(typename T::KRegs& X, typename T::KRegs& Y,
+                                          const char* kA, const char* kB, int r, int c) {
+    const char* ku = (r >> 3) ? kB : kA;
+    const int tok = 8 * ((r >> 2) & 1) + (r & 3);
+#pragma unroll
+    for (int i = 0; i < T::KL; ++i) {
+        X.k[i] = ld16(ku + ((4 * i + c) * kBS + tok) * 16);
+        Y.k[i] = ld16(ku + ((4 * i + c) * kBS + tok + 4) * 16);
+    }
+}
 
 template <int KIND> struct QType { using T = uint16_t; };   // bf16 bits
 template <> struct QType<KV_F32> { using T = float; };

@@ -56,3 +56,13 @@ def test_no_scratch_spills(device_asm):
         sizes = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
         assert sizes, f"{name}: no kernel descriptors found"
         assert all(int(x) == 0 for x in sizes), f"{name}: a kernel uses scratch ({sizes})"
+
+
+def test_copy_bases_not_sign_extended(device_asm):
+    """The prefill kernel's global-to-LDS copies take a 64-bit scalar base
+    assembled from two uniform 32-bit halves; widening the low half as a
+    signed value (s_bfe_i64 of the low word) would put 0xffffffff in the high
+    word of every address whose low word has bit 31 set."""
+    text = device_asm["prefill.hip"]
+    assert "global_load_lds_dwordx4" in text
+    assert not re.search(r"^\s*s_bfe_i64\b", text, re.M), "sign-extended 64-bit value in prefill"
