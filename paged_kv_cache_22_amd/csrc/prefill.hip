@@ -99,7 +99,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     const int ubeg = ranged ? (int)blockIdx.z * (a.key_range / kBS) : 0;
     const int kend = ranged ? min(L, ((int)blockIdx.z + 1) * a.key_range) : L;
     const int nrho = qlen * G;
-    const int rho_wg = blockIdx.y * (16 * NC * kWaves);
+    // Row tiles later in a causal chunk see more keys.  The second half of
+    // the grid's row tiles runs in reverse order, so workgroups y and
+    // y + ny/2 -- placed on one compute unit when the dispatcher fills the
+    // units in order twice over -- hold a long and a short tile.
+    const int ny = gridDim.y, yh = ny / 2;
+    const int ytile = ((int)blockIdx.y < yh || (ny & 1)) ? (int)blockIdx.y
+                                                         : ny - 1 - ((int)blockIdx.y - yh);
+    const int rho_wg = ytile * (16 * NC * kWaves);
     if (rho_wg >= nrho) return;  // uniform
     if (!ranged && ctx < 0) {
         // fewer cached tokens than queries (an idle sequence has none): the
@@ -237,11 +244,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
                 for (int e = 0; e < 8; ++e)
                     if (!unit_ok || kp0 + e > pos[ct]) t[e] = -INFINITY;
             }
-            float bm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                             fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-            bm = group_max4(bm);
-            const float mn = fmaxf(m[ct], bm);
-            if (__ballot((mn - m[ct]) * C > kRescaleLog2)) {
+            // each lane tests its own 8 scores against the column's running
+            // max; only when one of them jumps by more than the threshold
+            // (which is when the column max does) is the column max reduced
+            // over the lane groups and the state rescaled
+            const float bm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                                   fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+            if (__ballot((bm - m[ct]) * C > kRescaleLog2)) {
+                const float mn = fmaxf(m[ct], group_max4(bm));
                 const float alpha = fast_exp2((m[ct] - mn) * C);
                 accl[ct] *= alpha;
 #pragma unroll
