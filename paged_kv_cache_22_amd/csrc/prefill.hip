@@ -75,9 +75,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     constexpr int kCopies = UB / 1024;                       // 1 KiB copies per unit
     static_assert(UB % 1024 == 0 && kCopies * 4 % kWaves == 0, "whole copies per wave");
     constexpr int kPerWave = kCopies * 4 / kWaves;           // copies per wave and step
-    // a stage: K of unit A, kKPad bytes, K of unit B, V of unit A, V of unit B
-    constexpr int kOffKB = UB + T::kKPad, kOffVA = 2 * UB + T::kKPad, kOffVB = 3 * UB + T::kKPad;
-    constexpr int kStage = 4 * UB + T::kKPad;
+    // a stage: K of unit A, K of unit B, V of unit A, V of unit B
+    constexpr int kOffKB = UB, kOffVA = 2 * UB, kOffVB = 3 * UB;
+    constexpr int kStage = 4 * UB;
     constexpr int kStages = kStage * 3 <= 64 * 1024 ? 3 : 2;
     static_assert(kStage * kStages <= 64 * 1024, "LDS ring fits 64 KiB");
     __shared__ __attribute__((aligned(16))) char stage[kStages][kStage];
@@ -167,15 +167,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     // Copy k of this wave in a step is copy q = w + kWaves * k of the step's
     // 4 * kCopies: region q / kCopies (K of A, K of B, V of A, V of B), its
     // KiB q % kCopies.  voff: the lane's byte in the block tile (unit 0), as
-    // the region's layout in LDS asks (K verbatim, V by v_slot_hbm); fixed
-    // for the whole loop.
+    // the region's layout in LDS asks (K by k_lds_hbm, V by v_slot_hbm);
+    // fixed for the whole loop.
     uint32_t voff[kPerWave];
 #pragma unroll
     for (int k = 0; k < kPerWave; ++k) {
         const int q = w + kWaves * k, reg = q / kCopies;
         const int b = (q % kCopies) * 1024 + lane * 16;   // byte of the unit's LDS copy
-        voff[k] = reg < 2 ? (uint32_t)((b / (kBS * 16)) * (BS * 16) + b % (kBS * 16))
-                          : (uint32_t)T::v_slot_hbm(b / 16);
+        voff[k] = reg < 2 ? (uint32_t)k_lds_hbm<T, BS>(b) : (uint32_t)T::v_slot_hbm(b / 16);
     }
     const int nsteps = (nblk - ubeg + 1) / 2;
     // the physical blocks of step t's units (a missing second unit re-reads

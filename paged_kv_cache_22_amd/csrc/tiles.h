@@ -34,13 +34,18 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 // product X is token 8(c & 1) + e of unit c >> 1, and product Y the same
 // tokens + 4.  A lane's 8 weights then pair with one contiguous 8-token
 // piece of a V row, so the output product reads its operand in one piece:
-//   KRegs / load_k_xy    the K operands of X and Y from the staged units (K
-//                        keeps its HBM layout in LDS; unit B starts kKPad
-//                        bytes past unit A's end, so the 16 rows one read
-//                        touches hit distinct banks)
+//   KRegs / load_k_xy    the K operands of X and Y from the staged units: a
+//                        unit's LDS copy holds the rows of X, then those of
+//                        Y, each as [chunk][8 rows][16 bytes]; k_lds_hbm maps
+//                        a byte of that copy to its place in the block tile
 //   v_slot_hbm           where the 16-byte piece of LDS slot s of a staged V
-//                        unit comes from in the block tile (the slot order
-//                        swizzles pieces across banks)
+//                        unit comes from in the block tile
+// Both layouts are free of LDS bank conflicts for 16-byte reads, which gfx950
+// serves 16 lanes at a time -- lanes 0-7 with 24-31 and 8-15 with 16-23, the
+// same in the upper half-wave -- two lanes of one such pass conflicting when
+// they hit the same 16-byte slot of a 256-byte bank row (measured with the
+// SQ_LDS_BANK_CONFLICT counter on read patterns, then checked against the
+// kernels' own counts).
 //   VOp / load_v_xy      the lane's 8-token piece of dim rows 16n + r
 //   mask_v_xy            zero the V of tokens at or past `valid`
 //   pv_xy  acc[n] += V^T . P^T over the 32 tokens; lsum2 the weights' sums
@@ -70,17 +75,12 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
     __device__ static void settle(Regs&) {}   // loads land in MFMA layout
     struct KRegs { u32x4 k[KL]; };
-    static constexpr int kKPad = 64;
-    // V slot s = 2 * row + (h ^ ((row >> 3) & 1)) holds tokens 8h..8h+7 of dim row
-    __device__ static int v_slot_hbm(int slot) {
-        const int row = slot >> 1, h = (slot & 1) ^ ((row >> 3) & 1);
-        return row * (BS * 2) + h * 16;
-    }
+    // V slot s = 2 * row + h holds tokens 8h..8h+7 of dim row
+    __device__ static int v_slot_hbm(int slot) { return (slot >> 1) * (BS * 2) + (slot & 1) * 16; }
     struct VOp { u32x4 v[NT]; };
     __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
-        const int sw = (c & 1) ^ ((r >> 3) & 1);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) V.v[n] = ld16(vu + (2 * (16 * n + r) + sw) * 16);
+        for (int n = 0; n < NT; ++n) V.v[n] = ld16(vu + (2 * (16 * n + r) + (c & 1)) * 16);
     }
     __device__ static void mask_v_xy(VOp& V, int c, int valid) {
         const int t0 = 8 * (c & 1);
@@ -169,7 +169,6 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
         for (int m = 0; m < NT / 4; ++m) group_transpose4(R.v + 4 * m);
     }
     struct KRegs { u32x4 k[KL]; };
-    static constexpr int kKPad = 64;
     // V slot s is the unit's 16-token row of dim s (one 16-byte piece)
     __device__ static int v_slot_hbm(int slot) { return slot * BS; }
     struct VOp { u32x2 v[NT]; };   // codes of tokens 8(c & 1) .. +7
@@ -256,7 +255,6 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
     }
     __device__ static void settle(Regs&) {}
     struct KRegs { u32x4 k[KL]; };
-    static constexpr int kKPad = 0;    // (keeps two fp32 stages of d = 128 within 64 KiB)
     // V slot s = 4 * row + j holds tokens 4j..4j+3 of dim row
     __device__ static int v_slot_hbm(int slot) { return (slot >> 2) * (BS * 4) + (slot & 3) * 16; }
     struct VOp { u32x4 a[NT], b[NT]; };   // tokens 8(c & 1) + 0..3 and + 4..7
@@ -326,20 +324,33 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
     }
 };
 
+// K of one staged unit in LDS: the rows of X (tokens 0-3 and 8-11), then
+// those of Y (tokens 4-7 and 12-15), each half [chunk][8 rows][16 bytes];
+// row rr of a half is token 8 * ((rr >> 2) & 1) + (rr & 3), + 4 in Y.
+// k_lds_hbm: the block-tile byte (unit 0) of LDS byte b of that copy.
+template <class T, int BS>
+__device__ __forceinline__ int k_lds_hbm(int b) {
+    constexpr int HK = T::kUnitBytes / 2;
+    const int xy = b / HK, bb = b % HK;
+    const int chunk = bb >> 7, rr = (bb >> 4) & 7;
+    const int tok = 8 * ((rr >> 2) & 1) + (rr & 3) + 4 * xy;
+    return chunk * (BS * 16) + tok * 16;
+}
+
 // K operands of the score products X and Y from two staged units (kA, kB:
-// their LDS copies, in the HBM layout).  Row 4c + e of X is token
-// 8(c & 1) + e of unit c >> 1, row 4c + e of Y token 8(c & 1) + 4 + e: lane
-// (r, c) reads chunk 4i + c of token 8((r >> 2) & 1) + (r & 3) (+ 4 for Y)
-// of unit r >> 3.
+// their LDS copies).  Row 4c + e of X is token 8(c & 1) + e of unit c >> 1,
+// row 4c + e of Y token 8(c & 1) + 4 + e: lane (r, c) reads chunk 4i + c of
+// row r & 7 of the X (Y) half of unit r >> 3.
 template <class T>
 __device__ __forceinline__ void load_k_xy(typename T::KRegs& X, typename T::KRegs& Y,
                                           const char* kA, const char* kB, int r, int c) {
+    constexpr int HK = T::kUnitBytes / 2;
     const char* ku = (r >> 3) ? kB : kA;
-    const int tok = 8 * ((r >> 2) & 1) + (r & 3);
 #pragma unroll
     for (int i = 0; i < T::KL; ++i) {
-        X.k[i] = ld16(ku + ((4 * i + c) * kBS + tok) * 16);
-        Y.k[i] = ld16(ku + ((4 * i + c) * kBS + tok + 4) * 16);
+        const int off = ((4 * i + c) * 8 + (r & 7)) * 16;
+        X.k[i] = ld16(ku + off);
+        Y.k[i] = ld16(ku + HK + off);
     }
 }
 
