@@ -36,7 +36,10 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
         const int qi = qh / H, hq = qh - qi * H;
         const int h = hq / G, col = qi * G + (hq - h * G);
         const size_t cols = (size_t)a.q_len * G;
-        const int2 info = L > 0 ? reinterpret_cast<const int2*>(a.piece_info)[b] : make_int2(0, 0);
+        // the record exists for every sequence slot (it is only written for
+        // non-empty ones): read it alongside the length, use it only if L > 0
+        const int2 rec = reinterpret_cast<const int2*>(a.piece_info)[b];
+        const int2 info = L > 0 ? rec : make_int2(0, 0);
         np = info.y;
         base = ((size_t)h * a.piece_slots + info.x) * cols + col;
         pstride = cols;
@@ -50,8 +53,19 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     const float* lse = a.part_lse + base;
     const float* po = a.part_out + base * D + lane * V;
 
-    float M = -INFINITY;
-    for (int p = lane; p < np; p += 64) M = fmaxf(M, lse[(size_t)p * pstride]);
+    // the first kAhead partials (lse and this lane's dims) are fetched
+    // together with the lse values the maximum needs, so a row with few
+    // partials costs one round trip after its record
+    constexpr int kAhead = 4;   // (the max below is written out for 4)
+    float l0[kAhead], o0[kAhead][V];
+#pragma unroll
+    for (int p = 0; p < kAhead; ++p) {
+        l0[p] = p < np ? lse[(size_t)p * pstride] : -INFINITY;
+#pragma unroll
+        for (int v = 0; v < V; ++v) o0[p][v] = p < np ? po[(size_t)p * pstride * D + v] : 0.f;
+    }
+    float M = fmaxf(fmaxf(l0[0], l0[1]), fmaxf(l0[2], l0[3]));   // the same in every lane
+    for (int p = kAhead + lane; p < np; p += 64) M = fmaxf(M, lse[(size_t)p * pstride]);
     M = wave_max(M);
 
     float acc[V];
@@ -59,8 +73,16 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeArgs a) {
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
     float den = 0.f;
     if (M != -INFINITY) {
+#pragma unroll
+        for (int p = 0; p < kAhead; ++p) {
+            if (p >= np) break;
+            const float w = fast_exp2((l0[p] - M) * kLog2e);
+            den += w;
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] += w * o0[p][v];
+        }
 #pragma unroll 4
-        for (int p = 0; p < np; ++p) {
+        for (int p = kAhead; p < np; ++p) {
             // difference first: exactly 0 for the largest lse, whatever the
             // compiler fuses, so a lone partition passes through unchanged
             const float w = fast_exp2((lse[(size_t)p * pstride] - M) * kLog2e);
