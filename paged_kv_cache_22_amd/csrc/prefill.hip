@@ -12,12 +12,12 @@
 // waves owns 4 * NC tiles of one (chunk, kv-head); each wave owns NC tiles.
 // Key units go two at a time (a step) through a ring of kStages LDS stages,
 // filled by direct global-to-LDS copies (global_load_lds_dwordx4: 16 bytes
-// per lane, no registers, no LDS stores) issued kStages - 1 steps ahead, so
-// blocks that several chunks share -- a common prefix -- are served by L2
-// while earlier steps are computed.  Each step: wait for this wave's copies
-// of the step, one barrier (then every wave's copies have landed, and every
-// wave is done with the stage the next copy overwrites), issue the copies of
-// a later step, compute.  Per step and column tile: S^T = K . Q^T on MFMA in
+// per lane, no registers, no LDS stores) issued ahead of use, so blocks that
+// several chunks share -- a common prefix -- are served by L2 while earlier
+// steps are computed.  Steps go in groups of one or two: wait for this
+// wave's copies of the group, one barrier (then every wave's copies have
+// landed, and every wave is done with the stages the next copies
+// overwrite), issue the copies of a later group, compute.  Per step and column tile: S^T = K . Q^T on MFMA in
 // two products X and Y whose rows give each lane 8 consecutive tokens of one
 // unit, online softmax per column (base 2), then O^T += V^T . P^T with each
 // lane's V operand one 16-byte piece; the weights' column sums go through the
@@ -78,8 +78,13 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     // a stage: K of unit A, K of unit B, V of unit A, V of unit B
     constexpr int kOffKB = UB, kOffVA = 2 * UB, kOffVB = 3 * UB;
     constexpr int kStage = 4 * UB;
-    constexpr int kStages = kStage * 3 <= 64 * 1024 ? 3 : 2;
+    // Steps are consumed in groups of kGroup under one barrier: two when four
+    // stages fit in 64 KiB of LDS (the next group's copies fly while a group
+    // is computed), else one, with copies kStages - 1 steps ahead.
+    constexpr int kGroup = kStage * 4 <= 64 * 1024 ? 2 : 1;
+    constexpr int kStages = kGroup == 2 ? 4 : kStage * 3 <= 64 * 1024 ? 3 : 2;
     static_assert(kStage * kStages <= 64 * 1024, "LDS ring fits 64 KiB");
+    static_assert(kStages - 2 * kGroup >= 0 && kStages - 2 * kGroup <= 1, "copies in flight past a group");
     __shared__ __attribute__((aligned(16))) char stage[kStages][kStage];
 
     const int tid = threadIdx.x;
@@ -233,10 +238,17 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         const bool diag = jB >= full_end || !needB;
         const bool unit_ok = (c >> 1) == 0 || needB;
         const int kp0 = (jA + (c >> 1)) * kBS + 8 * (c & 1);   // key position of this lane's t[0]
+        // the score products of every column tile first (independent MFMA
+        // chains back to back), then each tile's softmax and output product
+        f32x4 sxa[NC], sya[NC];
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            const f32x4 sx = T::qk(X, Q[ct]);   // raw scores, as in decode
-            const f32x4 sy = T::qk(Y, Q[ct]);
+            sxa[ct] = T::qk(X, Q[ct]);   // raw scores, as in decode
+            sya[ct] = T::qk(Y, Q[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            const f32x4 sx = sxa[ct], sy = sya[ct];
             float t[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
             if (diag) {
 #pragma unroll
@@ -271,29 +283,37 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         }
     };
 
-    // prologue: steps 0 .. kStages-2 in flight
+    // prologue: steps 0 .. kStages-kGroup-1 in flight
     int pa = 0, pb = 0;
     phys_of(0, pa, pb);
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) {
+    for (int t = 0; t < kStages - kGroup; ++t) {
         if (t < nsteps) {
             copy_step(t, pa, pb);
             if (t + 1 < nsteps) phys_of(t + 1, pa, pb);
         }
     }
-    for (int s = 0; s < nsteps; ++s) {
-        // this wave's copies of step s are done once at most the later
-        // steps' copies (issued before this point) are outstanding
-        if (kStages == 3 && s + 1 < nsteps) wait_copies<kPerWave>();
+    for (int s = 0; s < nsteps; s += kGroup) {
+        // this wave's copies of the group's steps are done once at most the
+        // copies of later steps issued so far (kStages - 2 * kGroup steps,
+        // fewer at the end) are outstanding
+        if (kStages - 2 * kGroup == 1 && s + kGroup < nsteps) wait_copies<kPerWave>();
         else wait_copies<0>();
         barrier_lds();
-        const int t = s + kStages - 1;
-        if (t < nsteps) {
-            copy_step(t, pa, pb);     // overwrites the stage step s - 1 used
-            if (t + 1 < nsteps) phys_of(t + 1, pa, pb);
+        // the next copies overwrite the stages the previous group used
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            const int t = s + kStages - kGroup + i;
+            if (t < nsteps) {
+                copy_step(t, pa, pb);
+                if (t + 1 < nsteps) phys_of(t + 1, pa, pb);
+            }
         }
-        const int j0 = ubeg + 2 * s;
-        if (j0 < w_nblk) consume(s % kStages, j0);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            const int j0 = ubeg + 2 * (s + i);
+            if (s + i < nsteps && j0 < w_nblk) consume((s + i) % kStages, j0);
+        }
     }
 
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
