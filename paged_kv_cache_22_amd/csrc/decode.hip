@@ -326,19 +326,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
 // and the first piece's workgroup of kv-head 0 records (first slot, count)
 // for the merge.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
+// inclusive prefix sum over the wave's 64 lanes: DPP row shifts within each
+// 16-lane row, then row broadcasts carry the row totals upward (no LDS)
 __device__ __forceinline__ int wave_incl_scan_i(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
     return x;
 }
 
@@ -358,12 +354,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
     const int cols = (MQ ? a.q_len : 1) * G;   // output rows of one (piece, kv-head)
 
     // W: every wave sums ceil(L / 16) over the batch, 64 sequences at a time
-    // (all bookkeeping below is wave-uniform: scalar registers)
+    // (all bookkeeping below is wave-uniform: scalar registers); the first 64
+    // lengths stay in a register, so a batch of up to 64 sequences is read once
+    const int len0 = lane < B ? a.seq_lens[lane] : 0;
+    auto lens_at = [&](int c0) { return c0 == 0 ? len0 : (c0 + lane < B ? a.seq_lens[c0 + lane] : 0); };
     int W = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) {
-        const int bb = c0 + lane;
-        W += __builtin_amdgcn_readfirstlane(wave_sum_i(bb < B ? (a.seq_lens[bb] + kBS - 1) / kBS : 0));
-    }
+    for (int c0 = 0; c0 < B; c0 += 64)
+        W += __builtin_amdgcn_readlane(wave_incl_scan_i((lens_at(c0) + kBS - 1) / kBS), 63);
     // with fewer units than workgroups only the first W split (one unit
     // each): every split in use then owns at least one unit, so the splits
     // from a sequence's first to its last all hold a piece of it
@@ -374,10 +371,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
     // the sequence holding unit `start`, and the units before it
     int b = 0, cum = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
-        const int bb = c0 + lane;
-        const int n = bb < B ? (a.seq_lens[bb] + kBS - 1) / kBS : 0;
+        const int n = (lens_at(c0) + kBS - 1) / kBS;
         const int incl = wave_incl_scan_i(n);
-        const unsigned long long hit = __ballot(bb < B && cum + incl > start);
+        const unsigned long long hit = __ballot(c0 + lane < B && cum + incl > start);
         if (hit) {
             const int ln = __builtin_ctzll(hit);
             b = c0 + ln;
