@@ -340,11 +340,14 @@ def test_workspace_reuse_is_deterministic():
     compare(f64(outs[0]), oracle_decode(wl)[0], "bf16", "workspace reuse")
 
 
-def test_merge_on_oracle_partials():
-    """Standalone merge kernel on fp32 partials made by the oracle."""
+@pytest.mark.parametrize("P", [64, 256])
+def test_merge_on_oracle_partials(P):
+    """Standalone merge kernel on fp32 partials made by the oracle: 64
+    partitions at most (the workgroup-per-row merge) and 16 (the
+    wave-per-row merge)."""
     import paged_kv_cache_22_amd as pa
     rng = np.random.default_rng(140)
-    B, Hq, d_head, P = 6, 8, 128, 64
+    B, Hq, d_head = 6, 8, 128
     lens = np.array([0, 1, 64, 65, 1000, 4096], np.int32)
     pmax = -(-int(lens.max()) // P)
     o = rng.standard_normal((B, Hq, pmax, d_head)).astype(np.float32)
