@@ -52,7 +52,16 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 // ---------------------------------------------------------------------------
 template <int KIND, int D, int BS = kBS> struct Tile;
 
+// Decode loads a unit's K as whole 128-byte lines whatever the block size,
+// but a unit's V is a 16-token slice of each BS-token row: with 32- or
+// 64-token blocks the units of a block (taken by different waves at about
+// the same time) share every V line.  Those V loads keep the line in L2 for
+// its siblings instead of streaming it past (with streaming V loads the
+// 64-token batch fetched 1.46x its live bytes from HBM).
+template <int BS> constexpr bool kVStreamFor = BS == kBS;
+
 template <int D, int BS> struct Tile<KV_BF16, D, BS> {
+    static constexpr bool kVStream = kVStreamFor<BS>;
     static constexpr int kTileBytes = BS * D * 2;     // one (block, kv-head) tile
     static constexpr int kUnitBytes = kBS * D * 2;    // one 16-token unit
     static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 2;  // unit offsets in K runs / V rows
@@ -71,7 +80,10 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (BS * 2) + c * 8);
+        for (int n = 0; n < NT; ++n) {
+            const char* p = vt + (16 * n + r) * (BS * 2) + c * 8;
+            R.v[n] = kVStream ? ldkv8(p) : ld8(p);
+        }
     }
     __device__ static void settle(Regs&) {}   // loads land in MFMA layout
     struct KRegs { u32x4 k[KL]; };
@@ -132,6 +144,7 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
 };
 
 template <int D, int BS> struct Tile<KV_FP8, D, BS> {
+    static constexpr bool kVStream = kVStreamFor<BS>;
     static constexpr int kTileBytes = BS * D;
     static constexpr int kUnitBytes = kBS * D;
     static constexpr int kUnitK = kBS * 16, kUnitV = kBS;
@@ -157,7 +170,8 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
         for (int m = 0; m < NT / 4; ++m) {
-            const u32x4 w = ldkv16(vt + (16 * (4 * m + c) + r) * BS);
+            const char* p = vt + (16 * (4 * m + c) + r) * BS;
+            const u32x4 w = kVStream ? ldkv16(p) : ld16(p);
             R.v[4 * m] = w.x;
             R.v[4 * m + 1] = w.y;
             R.v[4 * m + 2] = w.z;
@@ -233,6 +247,7 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
 };
 
 template <int D, int BS> struct Tile<KV_F32, D, BS> {
+    static constexpr bool kVStream = kVStreamFor<BS>;
     static constexpr int kTileBytes = BS * D * 4;
     static constexpr int kUnitBytes = kBS * D * 4;
     static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 4;
@@ -251,7 +266,10 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
 #pragma unroll
         for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (BS * 4) + c * 16);
+        for (int n = 0; n < NT; ++n) {
+            const char* p = vt + (16 * n + r) * (BS * 4) + c * 16;
+            R.v[n] = kVStream ? ldkv16(p) : ld16(p);
+        }
     }
     __device__ static void settle(Regs&) {}
     struct KRegs { u32x4 k[KL]; };
