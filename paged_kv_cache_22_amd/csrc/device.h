@@ -80,18 +80,13 @@ __device__ __forceinline__ void group_transpose4(unsigned x[4]) {
     }
 }
 
-// Reductions over the 16 lanes of one row (same c), by DPP-style xor shuffles.
+// Maximum over the 16 lanes of one row (same c), by xor shuffles.
 __device__ __forceinline__ float row_max16(float x) {
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
     return x;
 }
 
-__device__ __forceinline__ float row_sum16(float x) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
 
 // hardware exp2 / log2 (v_exp_f32, v_log_f32)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -142,24 +137,10 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 acc) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// a wave-uniform global pointer pinned to scalar registers: adding a lane's
-// 32-bit offset to it then selects the scalar-base form of the global load,
-// and the compiler cannot fold the lane part into a per-lane 64-bit address
-typedef const char __attribute__((address_space(1))) gchar;
-__device__ __forceinline__ gchar* uniform_ptr(const char* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ u32x4 ld16(gchar* p) {
-    return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
-}
 
-// 16-byte / 8-byte / 4-byte global loads (plain vector loads)
+// 16-byte / 8-byte global loads (plain vector loads)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
-__device__ __forceinline__ unsigned ld4(const void* p) { return *reinterpret_cast<const unsigned*>(p); }
 
 // loads of KV data, which every kernel reads exactly once: non-temporal, so
 // the stream of K/V tiles does not evict what is reused (tables, q, partials)
@@ -178,13 +159,6 @@ __device__ __forceinline__ u32x2 ldkv8(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 #else
     return ld8(p);
-#endif
-}
-__device__ __forceinline__ unsigned ldkv4(const void* p) {
-#if PA_KV_NONTEMPORAL
-    return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
-#else
-    return ld4(p);
 #endif
 }
 
