@@ -17,11 +17,13 @@
 // steps are computed.  Steps go in groups of one or two: wait for this
 // wave's copies of the group, one barrier (then every wave's copies have
 // landed, and every wave is done with the stages the next copies
-// overwrite), issue the copies of a later group, compute.  Per step and column tile: S^T = K . Q^T on MFMA in
-// two products X and Y whose rows give each lane 8 consecutive tokens of one
-// unit, online softmax per column (base 2), then O^T += V^T . P^T with each
-// lane's V operand one 16-byte piece; the weights' column sums go through the
-// MFMA too.  Steps wholly below a wave's diagonal skip the mask.
+// overwrite), issue the copies of a later group, compute.  Per step and column
+// tile: S^T = K . Q^T on MFMA in two products X and Y whose rows give each
+// lane 8 consecutive tokens of one unit, online softmax per column (base 2),
+// then O^T += V^T . P^T with each lane's V operand one 16-byte piece; the
+// weights' column sums go through the MFMA too.  Steps wholly below a wave's
+// diagonal skip the mask.  The weights of one column tile are computed while
+// the output products of the previous one run on the matrix cores.
 #include "device.h"
 #include "launch.h"
 #include "tiles.h"
@@ -89,7 +91,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
+    // wave index: uniform, and known to be below kWaves (which folds the
+    // copy bookkeeping below into constants where the wave does not matter)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & (kWaves - 1);
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
@@ -167,7 +171,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         (size_t)ch * a.max_blocks_per_seq;
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
-    const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
+    // bytes between consecutive physical blocks (a 32-bit quantity: Hkv tiles)
+    const uint32_t blk_stride = (uint32_t)Hkv * (uint32_t)T::kTileBytes;
 
     // Copy k of this wave in a step is copy q = w + kWaves * k of the step's
     // 4 * kCopies: region q / kCopies (K of A, K of B, V of A, V of B), its
@@ -186,19 +191,21 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     // the first, which the consumer masks); uniform, so scalar loads
     auto phys_of = [&](int t, int& pa, int& pb) {
         const int ja = ubeg + 2 * t, jb = min(ja + 1, nblk - 1);
-        pa = trow[ja >> kSubShift];
-        pb = trow[jb >> kSubShift];
+        pa = trow[(unsigned)ja >> kSubShift];
+        pb = trow[(unsigned)jb >> kSubShift];
     };
     auto copy_step = [&](int t, int pa, int pb) {
         const int ja = ubeg + 2 * t, jb = min(ja + 1, nblk - 1);
         char* st = stage[t % kStages];
+        const uint64_t oa = (uint64_t)(uint32_t)pa * blk_stride;   // block indices are >= 0
+        const uint64_t ob = (uint64_t)(uint32_t)pb * blk_stride;
 #pragma unroll
         for (int k = 0; k < kPerWave; ++k) {
             const int q = w + kWaves * k, reg = q / kCopies;
             const int j = (reg & 1) ? jb : ja;
             const int sub = j & ((1 << kSubShift) - 1);
             const char* base = (reg < 2 ? kbase + sub * T::kUnitK : vbase + sub * T::kUnitV) +
-                               (size_t)((reg & 1) ? pb : pa) * blk_stride;
+                               ((reg & 1) ? ob : oa);
             const int dst = (reg == 0 ? 0 : reg == 1 ? kOffKB : reg == 2 ? kOffVA : kOffVB) +
                             (q % kCopies) * 1024;
             copy16_to_lds(base, voff[k], lds_addr(st + dst));
@@ -239,28 +246,40 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         const bool unit_ok = (c >> 1) == 0 || needB;
         const int kp0 = (jA + (c >> 1)) * kBS + 8 * (c & 1);   // key position of this lane's t[0]
         // the score products of every column tile first (independent MFMA
-        // chains back to back), then each tile's softmax and output product
+        // chains back to back), then the softmax and output products
         f32x4 sxa[NC], sya[NC];
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
             sxa[ct] = T::qk(X, Q[ct]);   // raw scores, as in decode
             sya[ct] = T::qk(Y, Q[ct]);
         }
+        // in three passes over the column tiles -- causal mask, running max
+        // (with its rare rescale branch), then the weights and output products
+        // -- so that the last pass is one branch-free block in which the
+        // weights of one tile are computed while the products of the previous
+        // tile run on the matrix cores
+        float t[NC][8];
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            const f32x4 sx = sxa[ct], sy = sya[ct];
-            float t[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
-            if (diag) {
+            t[ct][0] = sxa[ct][0]; t[ct][1] = sxa[ct][1]; t[ct][2] = sxa[ct][2]; t[ct][3] = sxa[ct][3];
+            t[ct][4] = sya[ct][0]; t[ct][5] = sya[ct][1]; t[ct][6] = sya[ct][2]; t[ct][7] = sya[ct][3];
+        }
+        if (diag) {
+#pragma unroll
+            for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (!unit_ok || kp0 + e > pos[ct]) t[e] = -INFINITY;
-            }
+                    if (!unit_ok || kp0 + e > pos[ct]) t[ct][e] = -INFINITY;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
             // each lane tests its own 8 scores against the column's running
             // max; only when one of them jumps by more than the threshold
             // (which is when the column max does) is the column max reduced
             // over the lane groups and the state rescaled
-            const float bm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                                   fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+            const float* tc = t[ct];
+            const float bm = fmaxf(fmaxf(fmaxf(tc[0], tc[1]), fmaxf(tc[2], tc[3])),
+                                   fmaxf(fmaxf(tc[4], tc[5]), fmaxf(tc[6], tc[7])));
             if (__ballot((bm - m[ct]) * C > kRescaleLog2)) {
                 const float mn = fmaxf(m[ct], group_max4(bm));
                 const float alpha = fast_exp2((m[ct] - mn) * C);
@@ -269,6 +288,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
                 for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
                 m[ct] = mn;
             }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
             // exp2(t * C - m * C) as one FMA per weight: at the maximum it
             // leaves the rounding error of m * C, far below bf16's resolution,
             // so the packed weight is exactly 1 there and the normaliser (the
@@ -276,10 +298,24 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             const float mc = m[ct] * C;
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[e], C, -mc));
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[ct][e], C, -mc));
             const auto pk = T::pack_p2(p);
             T::pv_xy(V, pk, acc[ct]);
             T::lsum2(pk, accl[ct]);
+        }
+        if constexpr (KIND == KV_BF16 && D == 128 && NC == 2) {
+            // schedule of that block: the first tile's weights (about 22
+            // VALU and transcendental ops), then each of its NT + 1 products
+            // followed by 3 ops of the second tile's weights, then the second
+            // tile's products
+            constexpr int kValuTrans = 0x002 | 0x400, kMfma = 0x008;
+            __builtin_amdgcn_sched_group_barrier(kValuTrans, 22, 0);
+#pragma unroll
+            for (int i = 0; i < NT + 1; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kValuTrans, 3, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kMfma, NT + 1, 0);
         }
     };
 
