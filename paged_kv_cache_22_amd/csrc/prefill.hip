@@ -213,13 +213,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     };
 
     // m: running max (raw score units); accl: the weights' column sums,
-    // accumulated by MFMA (every element of a lane's accl holds its column's sum)
-    float m[NC];
+    // accumulated by MFMA (every element of a lane's accl holds its column's sum);
+    // thr = m + kRescaleLog2 / C, the score past which a rescale is due, and
+    // mc = m * C, both updated only when m changes
+    float m[NC], thr[NC], mcs[NC];
+    const float dthr = kRescaleLog2 / C;
     f32x4 accl[NC];
     f32x4 acc[NC][NT];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
         m[ct] = -INFINITY;
+        thr[ct] = -INFINITY;
+        mcs[ct] = -INFINITY;
         accl[ct] = zero4();
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[ct][n] = zero4();
@@ -278,15 +283,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             // (which is when the column max does) is the column max reduced
             // over the lane groups and the state rescaled
             const float* tc = t[ct];
-            const float bm = fmaxf(fmaxf(fmaxf(tc[0], tc[1]), fmaxf(tc[2], tc[3])),
-                                   fmaxf(fmaxf(tc[4], tc[5]), fmaxf(tc[6], tc[7])));
-            if (__ballot((bm - m[ct]) * C > kRescaleLog2)) {
+            // (nested so that it compiles to three max3 and one max)
+            const float bm = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(tc[0], tc[1]), tc[2]),
+                                               fmaxf(fmaxf(tc[3], tc[4]), tc[5])), tc[6]), tc[7]);
+            if (__ballot(bm > thr[ct])) {
                 const float mn = fmaxf(m[ct], group_max4(bm));
                 const float alpha = fast_exp2((m[ct] - mn) * C);
                 accl[ct] *= alpha;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
                 m[ct] = mn;
+                thr[ct] = mn + dthr;
+                mcs[ct] = mn * C;
             }
         }
         // Raised wave priority over that block: the compute unit's arbiter
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             // leaves the rounding error of m * C, far below bf16's resolution,
             // so the packed weight is exactly 1 there and the normaliser (the
             // sum of the packed weights) matches it
-            const float mc = m[ct] * C;
+            const float mc = mcs[ct];
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(t[ct][e], C, -mc));
