@@ -54,6 +54,36 @@ __device__ __forceinline__ float to_e4m3_range(float x, float scale) {
     return fminf(fmaxf(y, -448.0f), 448.0f);
 }
 
+// The same quotient without the division sequence.  Markstein's theorem: with
+// r = RN(1/s) and q within an ulp of x/s, RN(q + r * (x - s * q)) = RN(x/s),
+// the residual x - s * q being exact by fma.  It stays exact while it is a
+// normal number, which scales in [2^-60, 2^60] guarantee for every quotient
+// of magnitude 2^-12 or more; smaller quotients encode to a signed zero
+// whatever their last bits (copysign keeps the zero's sign, which the
+// correction would lose for x = -0).  Quotients past 2^16 saturate to 448
+// either way, so q is clamped there first, which also keeps an infinite x
+// from turning the residual into NaN.  Checked on the device against the
+// division for every bf16 input and 1.5e10 random fp32 inputs over 109
+// scales (powers of two, their neighbours, amax / 448 values): the same fp32
+// quotient wherever it is 2^-12 or more, the same code everywhere.
+struct Quotient {
+    float s, r;
+    bool fast;   // s in [2^-60, 2^60]; else the division
+};
+__device__ __forceinline__ Quotient make_quotient(float s) {
+    Quotient q;
+    q.s = s;
+    q.r = 1.0f / s;
+    q.fast = s >= 0x1p-60f && s <= 0x1p60f;
+    return q;
+}
+__device__ __forceinline__ float to_e4m3_range_fast(float x, const Quotient& d) {
+    const float q = fminf(fmaxf(x * d.r, -65536.0f), 65536.0f);
+    const float e = fmaf(-q, d.s, x);
+    const float y = __builtin_copysignf(fmaf(e, d.r, q), x);
+    return fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
 __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float d) {
     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
@@ -167,12 +197,23 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
             unpack_row<IN, X>(vraw[i], vx);
             const float ksc = a.k_scale[h];
             const float vsc = a.v_scale[h];
+            const Quotient kd = make_quotient(ksc), vd = make_quotient(vsc);
+            if (kd.fast && vd.fast) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                kw[q] = pack_fp8x4(to_e4m3_range(kx[4 * q], ksc), to_e4m3_range(kx[4 * q + 1], ksc),
-                                   to_e4m3_range(kx[4 * q + 2], ksc), to_e4m3_range(kx[4 * q + 3], ksc));
-                vw[q] = pack_fp8x4(to_e4m3_range(vx[4 * q], vsc), to_e4m3_range(vx[4 * q + 1], vsc),
-                                   to_e4m3_range(vx[4 * q + 2], vsc), to_e4m3_range(vx[4 * q + 3], vsc));
+                for (int q = 0; q < 4; ++q) {
+                    kw[q] = pack_fp8x4(to_e4m3_range_fast(kx[4 * q], kd), to_e4m3_range_fast(kx[4 * q + 1], kd),
+                                       to_e4m3_range_fast(kx[4 * q + 2], kd), to_e4m3_range_fast(kx[4 * q + 3], kd));
+                    vw[q] = pack_fp8x4(to_e4m3_range_fast(vx[4 * q], vd), to_e4m3_range_fast(vx[4 * q + 1], vd),
+                                       to_e4m3_range_fast(vx[4 * q + 2], vd), to_e4m3_range_fast(vx[4 * q + 3], vd));
+                }
+            } else {  // scales outside [2^-60, 2^60]: the division itself
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    kw[q] = pack_fp8x4(to_e4m3_range(kx[4 * q], ksc), to_e4m3_range(kx[4 * q + 1], ksc),
+                                       to_e4m3_range(kx[4 * q + 2], ksc), to_e4m3_range(kx[4 * q + 3], ksc));
+                    vw[q] = pack_fp8x4(to_e4m3_range(vx[4 * q], vsc), to_e4m3_range(vx[4 * q + 1], vsc),
+                                       to_e4m3_range(vx[4 * q + 2], vsc), to_e4m3_range(vx[4 * q + 3], vsc));
+                }
             }
         } else {
             // bf16 / fp32: the input bits themselves (no arithmetic)

@@ -147,6 +147,100 @@ def test_fp8_ties_and_saturation(in_dtype):
     assert_same(vc, ev, f"ties {in_dtype} V")
 
 
+def _scale_sets():
+    """Two sets of 8 per-head scales: powers of two and their fp32
+    neighbours (significands of all ones and of 1 + ulp, where a quotient
+    through the reciprocal is hardest to round), amax / 448 values, and
+    scales far from 1, two of them outside [2^-60, 2^60]."""
+    nx = np.nextafter
+    f = np.float32
+    a = [f(1.0), f(2.0 ** -7), nx(f(2.0 ** -7), f(0)), nx(f(8.0), f(100)), f(3.0 / 448), f(0.1),
+         f(2.7 / 448), f(7.0)]
+    b = [nx(f(1.0), f(0)), f(2.0 ** 20), f(2.0 ** -70), nx(f(2.0 ** -20), f(1)), f(1.0 / 3),
+         f(5.5 / 448), f(123.456), f(2.0 ** 70)]   # 2^-70, 2^70: outside the fast quotient's range
+    return np.array(a, np.float32), np.array(b, np.float32)
+
+
+def _quant_workload(key, value, in_dtype, k_scale, v_scale, name):
+    T, hkv, d = key.shape
+    slots = np.arange(T, dtype=np.int32)
+    nb = -(-T // 16)
+    wl = W.write_workload(seed=9, slot_mapping=slots, num_kv_heads=hkv, head_dim=d,
+                          in_dtype=in_dtype, kv_dtype="fp8", num_blocks=nb, name=name)
+    wl.key, wl.value = key, value
+    wl.k_scale, wl.v_scale = k_scale, v_scale
+    return wl
+
+
+def test_fp8_quantise_every_bf16_value():
+    """Every bf16 bit pattern except the NaNs, quantised with each of 16
+    scales (8 per head for K, 8 for V): the codes equal the oracle's
+    (e4m3fn of the correctly rounded fp32 quotient), so the kernel's quotient
+    matches the true division wherever it can move a code.  NaN inputs are
+    outside the write's contract."""
+    bits = np.arange(65536, dtype=np.uint32)
+    nan = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+    vals = bits[~nan].astype(np.uint16)
+    d, hkv = 128, 8
+    rows = -(-vals.size // d)
+    flat = np.zeros(rows * d, np.uint16)
+    flat[:vals.size] = vals
+    flat = flat.reshape(rows, d)
+    key = np.repeat(flat[:, None, :], hkv, axis=1)                       # every value in every head
+    value = np.repeat(np.roll(flat, 37, axis=0)[:, None, :], hkv, axis=1)
+    ks, vs = _scale_sets()
+    wl = _quant_workload(np.ascontiguousarray(key), np.ascontiguousarray(value), "bf16", ks, vs,
+                         "every bf16 value")
+    kc, vc = run(wl)
+    ek, ev = expected(wl)
+    assert_same(kc, ek, "every bf16 value K")
+    assert_same(vc, ev, "every bf16 value V")
+
+
+def test_fp8_quantise_near_rounding_midpoints():
+    """fp32 inputs whose quotient lands within 3 fp32 ulps of an e4m3
+    rounding midpoint (every midpoint between neighbouring codes, the one
+    between 0 and the smallest subnormal, and 464 past the largest code),
+    both signs, for each head's scale: where the fp32 rounding of the
+    quotient decides the code."""
+    table = oracle.fp8_e4m3.table()[:0x7F].astype(np.float64)
+    mids = np.concatenate([(table[:-1] + table[1:]) / 2, [464.0]])
+    d, hkv = 128, 8
+    ks, vs = _scale_sets()
+
+    def rows_for(scales):
+        per_head = []
+        for sc in scales:
+            x0 = (mids * np.float64(sc)).astype(np.float32)
+            xs = [x0]
+            up, dn = x0.copy(), x0.copy()
+            for _ in range(3):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+                xs += [up, dn]
+            v = np.concatenate(xs)
+            v = np.concatenate([v, -v]).astype(np.float32)
+            per_head.append(v)
+        n = max(v.size for v in per_head)
+        T = -(-n // d)
+        out = np.zeros((T, hkv, d), np.float32)
+        for h, v in enumerate(per_head):
+            col = np.zeros(T * d, np.float32)
+            col[:v.size] = v
+            out[:, h, :] = col.reshape(T, d)
+        return out
+
+    key, value = rows_for(ks), rows_for(vs)
+    T = max(key.shape[0], value.shape[0])
+    key = np.concatenate([key, np.zeros((T - key.shape[0], hkv, d), np.float32)])
+    value = np.concatenate([value, np.zeros((T - value.shape[0], hkv, d), np.float32)])
+    wl = _quant_workload(key, value, "f32", ks, vs, "near midpoints")
+    kc, vc = run(wl)
+    ek, ev = expected(wl)
+    assert_same(kc, ek, "near midpoints K")
+    assert_same(vc, ev, "near midpoints V")
+
+
 @pytest.mark.parametrize("in_dtype,kv_dtype", [("bf16", "bf16"), ("bf16", "fp8")])
 def test_strided_views_of_fused_projection(in_dtype, kv_dtype):
     """key / value as column slices of a fused [T, (Hq + 2 Hkv) d] tensor."""
