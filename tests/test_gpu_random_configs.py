@@ -116,3 +116,109 @@ def test_random_prefill(i):
                                   wl.seq_lens, wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale,
                                   wl.v_scale)
     compare(f64(out), ref, c["kv"], what)
+
+
+N_WRITE = 12
+N_PREFIX = 12
+
+
+def write_case(i):
+    rng = np.random.default_rng([i, 983])
+    ind, kvd = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8")][int(rng.integers(4))]
+    bs = int(rng.choice([16, 32, 64]))
+    hkv = int(rng.choice([1, 2, 8, 10]))
+    d = int(rng.choice([64, 128]))
+    nb = int(rng.integers(2, 40))
+    cap = nb * bs
+    T = int(rng.integers(0, min(cap, 300) + 1))
+    # a chunk-like run at a random start, then scattered slots, all distinct
+    free = rng.permutation(cap)
+    run_len = int(rng.integers(0, T + 1))
+    start = int(rng.integers(0, cap - run_len + 1))
+    run = np.arange(start, start + run_len)
+    rest = free[~np.isin(free, run)][:T - run_len]
+    slots = np.concatenate([run, rest]).astype(np.int32)
+    if T:
+        slots[rng.random(T) < 0.1] = -1                      # padding tokens
+        if rng.random() < 0.5:
+            slots[rng.integers(T)] = cap + int(rng.integers(0, 50))   # outside the pool: skipped
+    return dict(ind=ind, kvd=kvd, bs=bs, hkv=hkv, d=d, nb=nb, slots=slots)
+
+
+@pytest.mark.parametrize("i", range(N_WRITE))
+def test_random_write(i):
+    """Cache writes byte for byte against the oracle (whole caches, so the
+    slots that must stay untouched are checked too)."""
+    import paged_kv_cache_22_amd as pa
+    from workloads.device import dev
+    c = write_case(i)
+    what = (f"write case {i}: {c['ind']}->{c['kvd']} bs={c['bs']} Hkv={c['hkv']} d={c['d']} "
+            f"NB={c['nb']} T={c['slots'].size}")
+    wl = W.write_workload(seed=7000 + i, slot_mapping=c["slots"], num_kv_heads=c["hkv"],
+                          head_dim=c["d"], in_dtype=c["ind"], kv_dtype=c["kvd"],
+                          num_blocks=c["nb"], block_size=c["bs"], name=f"random write {i}")
+    kc, vc = dev(wl.k_cache, wl.kv_dtype), dev(wl.v_cache, wl.kv_dtype)
+    print(f"[random] {what}", flush=True)
+    pa.write_kv(dev(wl.key, wl.in_dtype), dev(wl.value, wl.in_dtype), kc, vc, dev(wl.slot_mapping),
+                k_scale=dev(wl.k_scale), v_scale=dev(wl.v_scale))
+    torch.cuda.synchronize()
+    ek, ev = wl.k_cache.copy(), wl.v_cache.copy()
+    slots = wl.slot_mapping.copy()
+    slots[slots >= c["nb"] * c["bs"]] = -1                   # skipped by the library
+    oracle.write_kv(ek, ev, wl.key, wl.value, slots, wl.in_dtype, wl.kv_dtype,
+                    wl.k_scale, wl.v_scale)
+    for got, want, name in ((kc, ek, "K"), (vc, ev, "V")):
+        g = got.contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+        bad = int((g != np.ascontiguousarray(want).view(np.uint8).reshape(-1)).sum())
+        print(f"[parity] {what} {name}: {bad} bytes differ", flush=True)
+        assert bad == 0, f"{what}: {name} cache differs in {bad} bytes"
+
+
+def prefix_case(i):
+    rng = np.random.default_rng([i, 977])
+    c = _common(rng)
+    q_len = int(rng.choice([1, 1, 2, 4]))
+    while q_len * c["G"] > 16:
+        q_len //= 2
+    B = int(rng.integers(1, 10))
+    prefix = c["bs"] * int(rng.integers(0, 9))
+    lens = rng.integers(q_len, int(rng.choice([20, 200, 700])), size=B, endpoint=True)
+    if q_len == 1 and rng.random() < 0.3:
+        lens[rng.integers(B)] = 0                            # a sequence that is only the prefix
+    P = int(rng.choice([16, 64, 512]))
+    c.update(q_len=q_len, B=B, prefix=prefix, lens=lens.astype(np.int32), P=P)
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_PREFIX))
+def test_random_shared_prefix(i):
+    """The cascade (prefix key ranges, own-token partitions, merge) against
+    plain attention over each whole sequence."""
+    import paged_kv_cache_22_amd as pa
+    from workloads.device import dev
+    c = prefix_case(i)
+    what = (f"prefix case {i}: {c['kv']} d={c['d']} bs={c['bs']} Hkv={c['hkv']} G={c['G']} "
+            f"q_len={c['q_len']} prefix={c['prefix']} P={c['P']} own={c['lens'].tolist()}")
+    sp = W.shared_prefix_workload(seed=8000 + i, num_seqs=c["B"], num_q_heads=c["G"] * c["hkv"],
+                                  num_kv_heads=c["hkv"], head_dim=c["d"], prefix_len=c["prefix"],
+                                  len_lo=0, len_hi=0, q_dtype=c["qd"], kv_dtype=c["kv"],
+                                  q_len=c["q_len"] if c["q_len"] > 1 else 0, block_size=c["bs"],
+                                  suffix_lens=c["lens"], name=f"random prefix {i}")
+    wl = sp.full
+    print(f"[random] {what}", flush=True)
+    out = pa.decode_shared_prefix(dev(wl.q, wl.q_dtype), dev(wl.k_cache, wl.kv_dtype),
+                                  dev(wl.v_cache, wl.kv_dtype), dev(sp.prefix_table), sp.prefix_len,
+                                  dev(sp.suffix_table), dev(sp.suffix_lens),
+                                  max_seq_len=int(sp.suffix_lens.max()), partition_size=c["P"],
+                                  scale=wl.scale, k_scale=dev(wl.k_scale), v_scale=dev(wl.v_scale))
+    torch.cuda.synchronize()
+    if wl.q.ndim == 3:
+        ref = oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                            wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)[0]
+    else:
+        B, qn, Hq, d = wl.q.shape
+        ref, _ = oracle.prefill_chunk(wl.q.reshape(B * qn, Hq, d), np.arange(0, B * qn + 1, qn),
+                                      wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
+                                      wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
+        ref = ref.reshape(B, qn, Hq, d)
+    compare(f64(out), ref, c["kv"], what)
