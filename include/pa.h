@@ -130,7 +130,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * several sequences yields one partial per part, and the merge combines each
  * sequence's parts.  Every workgroup then streams the same number of bytes
  * whatever the mix of lengths.  Results equal the other modes up to the
- * rounding of the merge.
+ * rounding of the merge.  The mode pays when lengths vary widely or there
+ * are fewer (sequence, kv-head) pairs than resident workgroups; each
+ * sequence a range covers costs it a table load and a first-block load in
+ * series, so for large batches of short sequences (hundreds to thousands
+ * of sequences of a few hundred tokens) the one-pass mode is faster.
  * max_seq_len is the caller's host-side
  * bound on seq_lens; it sizes the grid.  A sequence of length 0 gets zeros.
  * scale is the softmax scale (1/sqrt(head_dim) for plain attention); it
