@@ -192,7 +192,8 @@ def test_fp8_quantise_every_bf16_value():
     wl = _quant_workload(np.ascontiguousarray(key), np.ascontiguousarray(value), "bf16", ks, vs,
                          "every bf16 value")
     kc, vc = run(wl)
-    ek, ev = expected(wl)
+    with np.errstate(over="ignore"):      # the largest values over small scales: inf, saturated to 448
+        ek, ev = expected(wl)
     assert_same(kc, ek, "every bf16 value K")
     assert_same(vc, ev, "every bf16 value V")
 
