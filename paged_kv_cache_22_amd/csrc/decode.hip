@@ -353,14 +353,26 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
     const int G = a.num_q_heads / a.num_kv_heads;
     const int cols = (MQ ? a.q_len : 1) * G;   // output rows of one (piece, kv-head)
 
-    // W: every wave sums ceil(L / 16) over the batch, 64 sequences at a time
-    // (all bookkeeping below is wave-uniform: scalar registers); the first 64
-    // lengths stay in a register, so a batch of up to 64 sequences is read once
-    const int len0 = lane < B ? a.seq_lens[lane] : 0;
-    auto lens_at = [&](int c0) { return c0 == 0 ? len0 : (c0 + lane < B ? a.seq_lens[c0 + lane] : 0); };
-    int W = 0;
-    for (int c0 = 0; c0 < B; c0 += 64)
-        W += __builtin_amdgcn_readlane(wave_incl_scan_i((lens_at(c0) + kBS - 1) / kBS), 63);
+    // W = sum of ceil(L / 16) over the batch.  Lane l owns the contiguous run
+    // of sequences [l*C, min(B, (l+1)*C)), C = ceil(B / 64), and sums its run
+    // with eight loads in flight at a time; one wave scan then gives W and
+    // the units before every run (all bookkeeping below is wave-uniform)
+    const int C = (B + 63) >> 6;
+    const int rb0 = lane * C;
+    int mine = 0, len0 = 0;
+    for (int k0 = 0; k0 < C; k0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int bb = rb0 + k0 + k;
+            v[k] = (k0 + k < C && bb < B) ? a.seq_lens[bb] : 0;
+        }
+        if (k0 == 0) len0 = v[0];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mine += (v[k] + kBS - 1) / kBS;
+    }
+    const int incl = wave_incl_scan_i(mine);
+    const int W = __builtin_amdgcn_readlane(incl, 63);
     // with fewer units than workgroups only the first W split (one unit
     // each): every split in use then owns at least one unit, so the splits
     // from a sequence's first to its last all hold a piece of it
@@ -368,25 +380,41 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
     if (s >= S) return;  // uniform
     const int start = (int)((long long)s * W / S), end = (int)((long long)(s + 1) * W / S);
 
-    // the sequence holding unit `start`, and the units before it
-    int b = 0, cum = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) {
-        const int n = (lens_at(c0) + kBS - 1) / kBS;
-        const int incl = wave_incl_scan_i(n);
-        const unsigned long long hit = __ballot(c0 + lane < B && cum + incl > start);
-        if (hit) {
-            const int ln = __builtin_ctzll(hit);
-            b = c0 + ln;
-            cum += __builtin_amdgcn_readlane(incl - n, ln);
-            break;
+    // the run holding unit `start` (the first lane whose inclusive sum
+    // passes it), then the sequence inside the run and the units before it;
+    // lw keeps the lengths of 64 consecutive sequences from lb (lane i holds
+    // L[lb + i]) for the piece loop
+    const int ln = __builtin_ctzll(__ballot(incl > start));
+    int cum = __builtin_amdgcn_readlane(incl - mine, ln);
+    const int rb = ln * C;
+    int b = rb, lb = 0, lw = len0;   // C == 1: lane i holds L[i] and run ln is sequence ln
+    if (C > 1) {
+        for (int k0 = 0; k0 < C; k0 += 64) {
+            const int i = k0 + lane;
+            const int Li = rb + i < B ? a.seq_lens[rb + i] : 0;
+            const int ni = (Li + kBS - 1) / kBS;
+            const int inc2 = wave_incl_scan_i(ni);
+            const unsigned long long hit = __ballot(i < C && rb + i < B && cum + inc2 > start);
+            if (hit) {
+                const int k = __builtin_ctzll(hit);
+                b = rb + k0 + k;
+                cum += __builtin_amdgcn_readlane(inc2 - ni, k);
+                lb = rb + k0;
+                lw = Li;
+                break;
+            }
+            cum += __builtin_amdgcn_readlane(inc2, 63);
         }
-        cum += __builtin_amdgcn_readlane(incl, 63);
     }
 
     const size_t slots = (size_t)gridDim.x + B;  // the merge's piece_slots
     int2* info = reinterpret_cast<int2*>(a.piece_info);
     for (int pos = start; pos < end && b < B; ++b) {
-        const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+        if (b - lb >= 64) {  // uniform: the next 64 lengths
+            lb = b;
+            lw = b + lane < B ? a.seq_lens[b + lane] : 0;
+        }
+        const int L = __builtin_amdgcn_readlane(lw, b - lb);
         const int n = (L + kBS - 1) / kBS;
         if (n == 0) continue;  // an empty sequence owns no unit (the merge writes its zeros)
         const int seg_end = min(end, cum + n);
