@@ -79,15 +79,9 @@ def test_batch_beyond_4096_sequences():
     print(f"[balanced] 8200 short sequences: total={wl.total_tokens}", flush=True)
     ref = oracle_decode(wl)
     got = f64(run_decode(Dev(wl), partition_size=BAL))
-    # Outputs of sequences this short reach |out| ~ 5, where rounding a
-    # result to bf16 alone moves it by up to half an ulp (2^-6 in [4, 8)):
-    # the bar is the graded 1e-2 plus that rounding, element by element.
-    err = np.abs(got - ref)
-    bound = 1e-2 + 2.0 ** -8 * np.abs(ref)
-    print(f"[parity] 8200 short sequences: max_abs_err={err.max():.3e} "
-          f"max|ref|={np.abs(ref).max():.3e} max(err/bound)={(err / bound).max():.3f}", flush=True)
-    assert np.isfinite(got).all()
-    assert (err <= bound).all(), f"error {err.max()} above 1e-2 + 2^-8 |ref|"
+    # outputs of sequences this short reach |out| ~ 5, where the bf16 output
+    # rounding alone is up to 2^-6: the bar adds it per element
+    compare(got, ref, "bf16", "8200 short sequences", out_rounding=True)
 
 
 def test_one_long_sequence_over_many_splits():

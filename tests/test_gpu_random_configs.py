@@ -5,8 +5,10 @@ queries per sequence, split mode (one pass, fixed partitions of any
 16-token multiple, balanced) and ragged lengths (idle sequences and the
 shortest legal ones included), so the parameters meet in combinations the
 targeted tests do not list.  Sizes stay small enough for the oracle to take
-a fraction of a second per case; the comparison is the graded bar plus the
-relative gate of every other parity test.
+a fraction of a second per case; the comparison is the graded bar, with the
+rounding of a bf16 output added per element (rows with few keys give outputs
+of magnitude 2-5, where that rounding alone reaches 2^-6), plus the relative
+gate of every other parity test.
 """
 import numpy as np
 import pytest
@@ -94,7 +96,7 @@ def test_random_decode(i):
         torch.cuda.synchronize()
         ref = oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
                             wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)[0]
-    compare(f64(out), ref, c["kv"], what)
+    compare(f64(out), ref, c["kv"], what, out_rounding=True)
 
 
 @pytest.mark.parametrize("i", range(N_PREFILL))
@@ -115,7 +117,7 @@ def test_random_prefill(i):
     ref, _ = oracle.prefill_chunk(wl.q, wl.cu_q_lens, wl.k_cache, wl.v_cache, wl.block_table,
                                   wl.seq_lens, wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale,
                                   wl.v_scale)
-    compare(f64(out), ref, c["kv"], what)
+    compare(f64(out), ref, c["kv"], what, out_rounding=True)
 
 
 N_WRITE = 12
@@ -221,4 +223,4 @@ def test_random_shared_prefix(i):
                                       wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
                                       wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
         ref = ref.reshape(B, qn, Hq, d)
-    compare(f64(out), ref, c["kv"], what)
+    compare(f64(out), ref, c["kv"], what, out_rounding=True)
