@@ -12,9 +12,9 @@ closed forms, a dense library routine, invariants and brute force
 (``tests/test_oracle_pins.py``; the fp8 encoder and the cache writer in
 ``tests/test_oracle_write_pins.py``).
 """
-from .attention import (decode, decode_partials, merge, prefill_chunk, gather_kv, attend,
-                        widen, round_to, items_for, write_kv)
+from .attention import (decode, decode_rows, decode_partials, merge, prefill_chunk,
+                        prefill_rows, gather_kv, attend, widen, round_to, write_kv)
 from . import fp8_e4m3
 
-__all__ = ["decode", "decode_partials", "merge", "prefill_chunk", "gather_kv", "attend",
-           "widen", "round_to", "items_for", "write_kv", "fp8_e4m3"]
+__all__ = ["decode", "decode_rows", "decode_partials", "merge", "prefill_chunk", "prefill_rows",
+           "gather_kv", "attend", "widen", "round_to", "write_kv", "fp8_e4m3"]

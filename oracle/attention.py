@@ -34,7 +34,7 @@ Storage dtypes: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 codes.
 from __future__ import annotations
 
 import math
-from typing import Iterable, Optional, Sequence, Tuple
+from typing import Iterable, Optional, Tuple
 
 import numpy as np
 
@@ -123,6 +123,23 @@ def _heads(Hq: int, Hkv: int) -> int:
     return Hq // Hkv
 
 
+def decode_rows(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: str,
+                kv_dtype: str, b: int, h: int, k_scale=None, v_scale=None):
+    """Decode attention of one (sequence b, kv-head h) pair: the G query heads
+    h*G .. h*G+G-1 of sequence b against its keys 0 .. L-1.  Returns
+    (out[G, d], lse[G]) in float64."""
+    Hq = q.shape[1]
+    G = _heads(Hq, k_cache.shape[1])
+    qf = widen(q[b, h * G:(h + 1) * G], q_dtype)
+    K, V = gather_kv(k_cache, v_cache, block_table[b], int(seq_lens[b]), h, kv_dtype,
+                     k_scale, v_scale)
+    out = np.empty((G, q.shape[2]))
+    lse = np.empty(G)
+    for g in range(G):
+        out[g], lse[g] = attend(qf[g], K, V, scale)
+    return out, lse
+
+
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: str,
            kv_dtype: str, k_scale=None, v_scale=None,
            items: Optional[Iterable[Tuple[int, int]]] = None):
@@ -134,16 +151,13 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: st
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     G = _heads(Hq, Hkv)
-    qf = widen(q, q_dtype)
     out = np.full((B, Hq, d), np.nan)
     lse = np.full((B, Hq), np.nan)
     todo = items if items is not None else [(b, h) for b in range(B) for h in range(Hkv)]
     for b, h in todo:
-        K, V = gather_kv(k_cache, v_cache, block_table[b], int(seq_lens[b]), h, kv_dtype,
-                         k_scale, v_scale)
-        for g in range(G):
-            j = h * G + g
-            out[b, j], lse[b, j] = attend(qf[b, j], K, V, scale)
+        out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G] = decode_rows(
+            q, k_cache, v_cache, block_table, seq_lens, scale, q_dtype, kv_dtype, b, h,
+            k_scale, v_scale)
     return out, lse
 
 
@@ -198,6 +212,30 @@ def merge(o_p: np.ndarray, lse_p: np.ndarray, seq_lens, partition_size: int):
     return out, lse
 
 
+def prefill_rows(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: float,
+                 q_dtype: str, kv_dtype: str, c: int, h: int, k_scale=None, v_scale=None):
+    """Causal prefill of one (chunk c, kv-head h) pair: the chunk's n query
+    rows, heads h*G .. h*G+G-1.  Query i sits at position ctx + i
+    (ctx = seq_lens[c] - n) and sees keys 0 .. ctx + i.  Returns
+    (out[n, G, d], lse[n, G]) in float64."""
+    Hq, d = q.shape[1], q.shape[2]
+    G = _heads(Hq, k_cache.shape[1])
+    q0, q1 = int(cu_q_lens[c]), int(cu_q_lens[c + 1])
+    L = int(seq_lens[c])
+    ctx = L - (q1 - q0)
+    if ctx < 0:
+        raise ValueError("seq_len smaller than the chunk")
+    qf = widen(q[q0:q1, h * G:(h + 1) * G], q_dtype)
+    K, V = gather_kv(k_cache, v_cache, block_table[c], L, h, kv_dtype, k_scale, v_scale)
+    out = np.empty((q1 - q0, G, d))
+    lse = np.empty((q1 - q0, G))
+    for i in range(q1 - q0):
+        visible = ctx + i + 1
+        for g in range(G):
+            out[i, g], lse[i, g] = attend(qf[i, g], K[:visible], V[:visible], scale)
+    return out, lse
+
+
 def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: float,
                   q_dtype: str, kv_dtype: str, k_scale=None, v_scale=None,
                   items: Optional[Iterable[Tuple[int, int]]] = None):
@@ -211,44 +249,35 @@ def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: 
     total_q, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     G = _heads(Hq, Hkv)
-    qf = widen(q, q_dtype)
     out = np.full((total_q, Hq, d), np.nan)
     lse = np.full((total_q, Hq), np.nan)
     n_chunks = len(seq_lens)
     todo = items if items is not None else [(c, h) for c in range(n_chunks) for h in range(Hkv)]
     for c, h in todo:
         q0, q1 = int(cu_q_lens[c]), int(cu_q_lens[c + 1])
-        L = int(seq_lens[c])
-        ctx = L - (q1 - q0)
-        if ctx < 0:
-            raise ValueError("seq_len smaller than the chunk")
-        K, V = gather_kv(k_cache, v_cache, block_table[c], L, h, kv_dtype, k_scale, v_scale)
-        for i in range(q1 - q0):
-            visible = ctx + i + 1
-            for g in range(G):
-                j = h * G + g
-                out[q0 + i, j], lse[q0 + i, j] = attend(qf[q0 + i, j], K[:visible],
-                                                        V[:visible], scale)
+        out[q0:q1, h * G:(h + 1) * G], lse[q0:q1, h * G:(h + 1) * G] = prefill_rows(
+            q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale, q_dtype, kv_dtype,
+            c, h, k_scale, v_scale)
     return out, lse
 
 
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
     """Round float64 results to the output storage type and widen back (for
-    comparing against values a kernel had to round): RNE to fp32, then to bf16."""
-    f = np.asarray(x, dtype=np.float32)
+    comparing against values a kernel had to round): round to nearest even to
+    fp32, then to bf16 (add half an ulp of the kept part, minus one unless the
+    kept part is odd, and drop the low 16 bits).  Overflow gives an infinity
+    of the right sign; a NaN stays a NaN."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        f = np.asarray(x, dtype=np.float32)
     if dtype == "f32":
         return f.astype(np.float64)
     if dtype == "bf16":
         bits = f.view(np.uint32).astype(np.uint64)
         lsb = (bits >> np.uint64(16)) & np.uint64(1)
         r = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-        return r.astype(np.uint32).view(np.float32).astype(np.float64)
+        out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+        return np.where(np.isnan(f), np.nan, out)
     raise ValueError(dtype)
-
-
-def items_for(seq_ids: Sequence[int], Hkv: int):
-    """All (sequence, kv-head) pairs of the given sequences."""
-    return [(int(b), h) for b in seq_ids for h in range(Hkv)]
 
 
 # ---------------------------------------------------------------------------

@@ -11,6 +11,26 @@ TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}          # graded max-abs error
 REL = {"f32": 2e-6, "bf16": 2.0 ** -7, "fp8": 2.0 ** -7}
 
 
+def pool():
+    """The oracle's process pool (all host cores, one BLAS thread each): the
+    full-size references in seconds instead of minutes."""
+    from oracle.pool import shared_pool
+    return shared_pool()
+
+
+def oracle_decode(wl, items=None):
+    """oracle.decode of a decode workload, over the pool."""
+    return pool().decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                         wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale, items=items)
+
+
+def oracle_prefill(wl, items=None):
+    """oracle.prefill_chunk of a prefill workload, over the pool."""
+    return pool().prefill_chunk(wl.q, wl.cu_q_lens, wl.k_cache, wl.v_cache, wl.block_table,
+                                wl.seq_lens, wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale,
+                                wl.v_scale, items=items)
+
+
 def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 

@@ -6,25 +6,15 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import Dev, compare, f64, run_decode, run_prefill
+from gpu_util import Dev, compare, f64, oracle_decode, oracle_prefill, run_decode, run_prefill
 
 pytestmark = pytest.mark.gpu
-
-
-def oracle_prefill(wl, items=None):
-    return oracle.prefill_chunk(wl.q, wl.cu_q_lens, wl.k_cache, wl.v_cache, wl.block_table,
-                                wl.seq_lens, wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale,
-                                wl.v_scale, items=items)
 
 
 # The normaliser is the sum of the weights as they enter the PV product
 # (bf16 for bf16 / fp8 KV), so the lse carries their rounding:
 # |error| <= ln(1 + 2^-9) ~ 1.95e-3.  fp32 weights stay fp32.
 LSE_TOL = {"f32": 1e-3, "bf16": 2e-3, "fp8": 2e-3}
-
-
-def rows_mask(ref):
-    return ~np.isnan(ref[..., 0])
 
 
 @pytest.mark.parametrize("kv,d_head", [("f32", 64), ("f32", 128), ("bf16", 128), ("bf16", 64),
@@ -73,22 +63,36 @@ def test_group_sizes(G):
     compare(f64(run_prefill(Dev(wl))), ref, "bf16", f"prefill G={G}")
 
 
-def test_c4_mixed_step():
+@pytest.fixture(scope="module")
+def c4():
+    """The mixed step at full size and its full oracle references: every
+    (sequence, kv-head) pair of the 16 decode rows and every (chunk, kv-head)
+    pair of the 4 chunks over the shared prefix."""
     wl = W.config4()
-    # decode rows of the mixed step
-    dd = Dev(wl.decode)
-    ref_d, _ = oracle.decode(wl.decode.q, wl.decode.k_cache, wl.decode.v_cache,
-                             wl.decode.block_table, wl.decode.seq_lens, wl.decode.scale,
-                             "bf16", "bf16")
-    compare(f64(run_decode(dd)), ref_d, "bf16", "C4 decode rows")
-    # prefill chunks over the shared 2048-token prefix (sampled (chunk, kv-head) pairs)
-    pre = wl.prefill
-    dp = Dev(pre)
-    got = f64(run_prefill(dp))
-    items = [(c, h) for c in range(4) for h in (0, 5)] + [(2, h) for h in (1, 2, 3, 4, 6, 7)]
-    ref, _ = oracle_prefill(pre, items)
-    compare(got, ref, "bf16", "C4 prefill sampled", mask=rows_mask(ref))
-    assert np.isfinite(got).all()
+    ref_d = oracle_decode(wl.decode)[0]
+    ref_p, ref_l = oracle_prefill(wl.prefill)
+    assert np.isfinite(ref_d).all() and np.isfinite(ref_p).all()
+    return wl, ref_d, ref_p, ref_l
+
+
+@pytest.mark.parametrize("P", [512, -1])
+def test_c4_mixed_step(c4, P):
+    """One mixed step as it runs in a serving step: pa_decode on the decode
+    rows, then pa_prefill_chunk on the chunks, back to back on one stream
+    with no synchronisation between; every output row against the oracle.
+    P: the decode rows' 512-token partitions or the balanced split."""
+    import paged_kv_cache_22_amd as pa
+    wl, ref_d, ref_p, ref_l = c4
+    dd, dp = Dev(wl.decode), Dev(wl.prefill)
+    dec, pre = wl.decode, wl.prefill
+    out_d = pa.decode(dd.q, dd.k, dd.v, dd.bt, dd.sl, max_seq_len=dec.max_seq_len,
+                      scale=dec.scale, partition_size=P)
+    out_p, lse_p = pa.prefill_chunk(dp.q, dp.cu, dp.k, dp.v, dp.bt, dp.sl, max_q_len=pre.max_q_len,
+                                    scale=pre.scale, want_lse=True)
+    torch.cuda.synchronize()
+    compare(f64(out_d), ref_d, "bf16", f"C4 decode rows P={P}")
+    compare(f64(out_p), ref_p, "bf16", "C4 prefill chunks, all rows")
+    assert np.abs(f64(lse_p) - ref_l).max() < LSE_TOL["bf16"]
 
 
 def test_causal_boundary_exact_selection():

@@ -26,7 +26,8 @@ from oracle import fp8_e4m3
 import workloads as W
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")
-FACTS = json.load(open(GOLD))
+with open(GOLD) as _f:
+    FACTS = json.load(_f)
 
 
 # ---------------------------------------------------------------------------
@@ -524,3 +525,65 @@ def test_mutation_scale_dropped(monkeypatch):
     orig = A.attend
     monkeypatch.setattr(A, "attend", lambda q, K, V, scale: orig(q, K, V, 1.0))
     assert not _pins_pass()
+
+
+# ---------------------------------------------------------------------------
+# round_to: fp64 results rounded to the output storage type
+# ---------------------------------------------------------------------------
+def _round_to_cases():
+    """fp32 bit patterns: random ones, exact ties (both parities of the kept
+    last bit), subnormals, the neighbourhood of the largest finite bf16, and
+    the special values."""
+    rng = np.random.default_rng(77)
+    rand = rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, 4000, dtype=np.uint64).astype(np.uint32) << np.uint32(16)) \
+        | np.uint32(0x8000)
+    sub = rng.integers(1, 2 ** 23, 4000, dtype=np.uint64).astype(np.uint32)
+    sub = np.concatenate([sub, sub | np.uint32(0x80000000)])
+    top = np.uint32(0x7F7F0000) + np.arange(0, 0x10000, 7, dtype=np.uint32)
+    top = np.concatenate([top, top | np.uint32(0x80000000), [np.uint32(0x7F7F8000)]])
+    special = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001,
+                        0x3F800000, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    return np.concatenate([rand, ties, sub, top, special]).astype(np.uint32).view(np.float32)
+
+
+def test_round_to_bf16_matches_torch_cast():
+    """oracle.round_to(x, "bf16") on fp32 values is round to nearest even to
+    bf16: bit for bit what torch's CPU cast gives, signed zeros, overflow to
+    infinity and NaN included."""
+    x = _round_to_cases()
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).float().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):    # signalling NaN patterns among the inputs
+        got = A.round_to(x.astype(np.float64), "bf16")
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), want[~nan].view(np.uint64))
+
+
+def test_round_to_worked_ties():
+    """bf16 keeps 7 fraction bits: 1 + 2^-8 lies halfway between 1 and
+    1 + 2^-7 and goes to the even one, 1; 1 + 3 * 2^-8 lies halfway between
+    1 + 2^-7 and 1 + 2^-6 and goes to 1 + 2^-6; just past a tie rounds up."""
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -(1 + 2.0 ** -8)])
+    assert list(A.round_to(x, "bf16")) == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0]
+
+
+def test_round_to_fp64_rounds_through_fp32():
+    """fp64 inputs are first rounded to fp32 (as the kernels hold them), then
+    to bf16: equal to torch casting float64 -> float32 -> bfloat16."""
+    rng = np.random.default_rng(78)
+    x = rng.standard_normal(100_000) * np.exp2(rng.integers(-30, 30, 100_000))
+    want = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(A.round_to(x, "bf16"), want)
+    assert np.array_equal(A.round_to(x, "f32"), x.astype(np.float32).astype(np.float64))
+
+
+def test_mutation_round_to_truncates(monkeypatch):
+    """A round_to that truncates instead of rounding fails the pin."""
+    def trunc(x, dtype):
+        f = np.asarray(x, dtype=np.float32)
+        b = f.view(np.uint32) & np.uint32(0xFFFF0000)
+        return b.view(np.float32).astype(np.float64)
+    monkeypatch.setattr(A, "round_to", trunc)
+    with pytest.raises(AssertionError):
+        test_round_to_bf16_matches_torch_cast()
