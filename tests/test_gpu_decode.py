@@ -304,8 +304,10 @@ def test_balanced_mode_depends_on_batch_only_within_rounding():
     depends on its batch-mates and on the device's occupancy, and its bits
     may change with the batch (the one-pass and fixed-partition modes are
     batch-invariant bit for bit: above).  Alone and in a batch, a sequence's
-    balanced results agree within the merge's rounding, 2^-8 of the largest
-    output, and both match the oracle."""
+    balanced results agree to one bf16 step -- the two fp32 results differ
+    by the merge's rounding, and where they straddle a rounding boundary of
+    the output they land one step apart, up to 2^-7 of the value -- and both
+    match the oracle."""
     import paged_kv_cache_22_amd as pa
     wl = W.decode_workload(seed=121, num_seqs=10, num_q_heads=32, num_kv_heads=8, head_dim=128,
                            len_lo=1, len_hi=6000, q_dtype="bf16", kv_dtype="bf16")
@@ -321,7 +323,7 @@ def test_balanced_mode_depends_on_batch_only_within_rounding():
         torch.cuda.synchronize()
         one = f64(one)[0]
         compare(one, ref[b], "bf16", f"balanced, sequence {b} alone")
-        assert np.abs(one - full[b]).max() <= 2.0 ** -8 * np.abs(ref[b]).max(), b
+        assert np.abs(one - full[b]).max() <= 2.0 ** -7 * np.abs(ref[b]).max(), b
         differ += int(not np.array_equal(one, full[b]))
     print(f"[balanced] {differ} of {wl.num_seqs} sequences change bits with the batch", flush=True)
 
