@@ -151,6 +151,34 @@ int pa_decode(void* out, const void* q, int q_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same arguments and results as pa_decode, without `workspace`, whose role a
+ * fixed buffer inside the library takes: PA_STATIC_WORKSPACE_BYTES of device
+ * memory per GPU, part of the library's code object, held by each GPU the
+ * library runs on until the process ends.  The call allocates nothing.
+ * Returns PA_ERR_WORKSPACE, before enqueuing anything, when
+ * pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+ * partition_size) exceeds the buffer (for 32 q-heads of 128 dims: the
+ * balanced mode up to about 3000 sequences; 512-token partitions up to
+ * 15 sequences of 128K tokens).  Every call on one GPU uses that GPU's one
+ * buffer, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls ordered on one stream are fine, calls that may overlap on
+ * one GPU (other streams, other threads) race and give wrong results.  The
+ * buffer's address is looked up on the first call with each device current
+ * (make that call, like the balanced mode's first call, outside capture).
+ */
+#define PA_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+int pa_decode_noalloc(void* out, const void* q, int q_dtype,
+                      const void* k_cache, const void* v_cache, int kv_dtype,
+                      const int32_t* block_table, int max_blocks_per_seq,
+                      const int32_t* seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                      int partition_size, int max_seq_len, void* stream);
+
+/*
  * Multi-query decode: each sequence has q_len queries, the newest q_len
  * tokens already in its cache, as when drafted tokens are verified in one
  * step (speculative decoding: in vllm-mblt 0.8.0, "Serve an EAGLE-3 Model",

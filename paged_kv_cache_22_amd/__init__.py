@@ -4,6 +4,7 @@ The computation lives in ``libpa.so`` (hand-written HIP kernels behind the C
 ABI of ``include/pa.h``); this package is its thin Python binding:
 
 * :func:`decode`            one query per sequence, optional split-KV + merge
+* :func:`decode_noalloc`    the same with the library's fixed device workspace
 * :func:`decode_partitions` the split-KV partition kernel alone
 * :func:`merge_partitions`  log-sum-exp merge of partition results
 * :func:`prefill_chunk`     causal chunked prefill over a paged context
@@ -12,12 +13,12 @@ Importing the package loads ``libpa.so`` and fails if it is not built
 (``python paged_kv_cache_22_amd/build.py``).
 """
 from ._binding import (LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALANCED, PAError, decode,
-                       decode_multi_query, decode_shared_prefix, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
+                       decode_noalloc, STATIC_WORKSPACE_BYTES, decode_multi_query, decode_shared_prefix, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
                        PA_STAGE_ALL,
                        decode_partitions, decode_workspace_size, lib, merge_partitions,
                        prefill_chunk, status_string, write_kv)
 
-__all__ = ["decode", "decode_multi_query", "decode_shared_prefix", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
+__all__ = ["decode", "decode_noalloc", "STATIC_WORKSPACE_BYTES", "decode_multi_query", "decode_shared_prefix", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
            "PA_STAGE_ALL", "decode_partitions", "merge_partitions", "prefill_chunk", "write_kv",
            "decode_workspace_size", "status_string", "PAError", "lib", "LIB_PATH",
            "PA_F32", "PA_BF16", "PA_FP8_E4M3", "PA_PARTITION_BALANCED"]

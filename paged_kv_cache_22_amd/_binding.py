@@ -27,6 +27,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f,
                        _vp, _vp, _i, _i, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i,
+                               _f, _vp, _vp, _i, _i, _vp]),
     "pa_decode_multi_query": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
                                    _i, _i, _f, _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "pa_decode_stages": (_i, [_vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
@@ -154,6 +156,29 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
                        int(partition_size), int(max_seq_len),
                        _dev(workspace, "workspace"), ws_bytes, _stream(q))
     _check("pa_decode", st)
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20   # PA_STATIC_WORKSPACE_BYTES
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int, out,
+                   scale: Optional[float] = None, partition_size: int = 0, k_scale=None,
+                   v_scale=None):
+    """pa_decode_noalloc: pa_decode with the library's fixed device workspace;
+    ``out`` (caller-owned, [B, Hq, d] in q's dtype) is written, nothing is
+    allocated."""
+    B, Hq, d, NB, Hkv, bs = _kv_dims(q, k_cache, v_cache)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.pa_decode_noalloc(_dev(out, "out"), _dev(q, "q"), _dtype_code(q, False),
+                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                               _dtype_code(k_cache, True), _dev(block_table, "block_table"),
+                               block_table.shape[1], _dev(seq_lens, "seq_lens"), B, Hq, Hkv, d,
+                               bs, NB, float(scale), _dev(k_scale, "k_scale"),
+                               _dev(v_scale, "v_scale"), int(partition_size), int(max_seq_len),
+                               _stream(q))
+    _check("pa_decode_noalloc", st)
     return out
 
 

@@ -344,6 +344,33 @@ int pa_decode(void* out, const void* q, int q_dtype, const void* k_cache, const 
                        workspace_bytes, stream);
 }
 
+static_assert(PA_STATIC_WORKSPACE_BYTES == pa::kStaticWorkspaceBytes,
+              "pa.h and the library agree on the fixed workspace size");
+
+int pa_decode_noalloc(void* out, const void* q, int q_dtype, const void* k_cache,
+                      const void* v_cache, int kv_dtype, const int32_t* block_table,
+                      int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                      int partition_size, int max_seq_len, void* stream) {
+    int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_blocks, scale, k_scale, v_scale, partition_size, max_seq_len);
+    if (st != PA_OK) return st;
+    if (num_seqs > 0 && !out) return PA_ERR_NULL;
+    if (!aligned16(out)) return PA_ERR_ALIGN;
+    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                                 partition_size);
+    if (need > PA_STATIC_WORKSPACE_BYTES) return PA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (num_seqs > 0 && need > 0 && pa::static_workspace(&ws, &ws_bytes) != 0) return PA_ERR_HIP;
+    return decode_impl(out, q, q_dtype, 1, k_cache, v_cache, kv_dtype, block_table,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, scale, k_scale, v_scale, partition_size, max_seq_len, ws,
+                       ws_bytes, stream);
+}
+
 int pa_decode_multi_query(void* out, const void* q, int q_dtype, int q_len, const void* k_cache,
                           const void* v_cache, int kv_dtype, const int32_t* block_table,
                           int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,

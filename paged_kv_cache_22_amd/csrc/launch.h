@@ -107,6 +107,14 @@ constexpr int kMaxBalancedSplits = 1024;
 // [1, kMaxBalancedSplits]); -1 if the runtime cannot tell.
 int balanced_splits(const DecodeArgs& a);
 
+// Bytes of the library's fixed device workspace (pa_decode_noalloc).
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+
+// The current device's copy of that workspace: its device address and size.
+// The address is looked up once per device (the first call with that device
+// current) and cached.  Returns 0, or the hipError_t of the lookup.
+int static_workspace(void** ptr, size_t* bytes);
+
 // Each returns 0 on success or the hipError_t of a failed launch.
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);

@@ -256,3 +256,33 @@ def test_stages_rejects():
     assert call(qn=8) == UNSUP                    # 8 x 4 columns: only the prefill route has them
     assert call(qn=0) == SHAPE
     assert call(ws=None) == WS
+
+
+def noalloc_call(**over):
+    a = dict(out=P, q=P, q_dtype=1, k=P, v=P, kv_dtype=1, bt=P, max_blocks=4096, sl=P,
+             num_seqs=2, hq=32, hkv=8, d=128, bs=16, nb=9000, scale=0.088, ks=None, vs=None,
+             part=16, max_len=65536, stream=None)
+    a.update(over)
+    return pa.lib.pa_decode_noalloc(a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv_dtype"],
+                                    a["bt"], a["max_blocks"], a["sl"], a["num_seqs"], a["hq"],
+                                    a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["ks"],
+                                    a["vs"], a["part"], a["max_len"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), WS),                                    # 4096 partitions x 2 seqs: 135 MB > 64 MiB
+    (dict(part=-1, num_seqs=3100, max_len=4096, max_blocks=256), WS),   # balanced, 3100 seqs
+    (dict(out=None), NULL), (dict(q_dtype=0), DTYPE), (dict(d=96), UNSUP),
+    (dict(out=P + 8), ALIGN), (dict(part=24), UNSUP),
+])
+def test_noalloc_rejects_before_launch(over, status):
+    assert noalloc_call(**over) == status
+
+
+def test_noalloc_buffer_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PA_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_WORKSPACE_BYTES == 64 << 20
+    assert pa.decode_workspace_size(2, 32, 128, 65536, 16) > B.STATIC_WORKSPACE_BYTES
+    assert pa.decode_workspace_size(3100, 32, 128, 4096, -1) > B.STATIC_WORKSPACE_BYTES
+    assert pa.decode_workspace_size(64, 32, 128, 4096, -1) < B.STATIC_WORKSPACE_BYTES

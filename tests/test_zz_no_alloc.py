@@ -1,0 +1,75 @@
+"""pa_decode_noalloc (pa_decode with the library's fixed device workspace,
+for callers that cannot allocate) through the C ABI: bit for bit the output
+of pa_decode with a caller-owned workspace, on two calls in a row, the
+second with a smaller batch (the fixed buffer still holds the first call's
+partials and piece records), in every decode mode; and the oracle's result
+within the graded tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import Dev, compare, f64, oracle_decode, run_decode
+
+pytestmark = pytest.mark.gpu
+BAL = -1   # PA_PARTITION_BALANCED
+
+
+def _noalloc(d, P):
+    import paged_kv_cache_22_amd as pa
+    wl = d.wl
+    out = torch.full_like(d.q, float("nan"))
+    pa.decode_noalloc(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                      partition_size=P, k_scale=d.ks, v_scale=d.vs, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("P", [BAL, 512, 0])
+def test_noalloc_equals_pa_decode_on_two_calls(P):
+    big = W.config2()
+    small = W.decode_workload(seed=301, num_seqs=7, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              len_lo=1, len_hi=3000, q_dtype="bf16", kv_dtype="bf16")
+    for wl in (big, small):
+        print(f"[noalloc] P={P} {wl.name}: B={wl.num_seqs} tokens={wl.total_tokens}", flush=True)
+        d = Dev(wl)
+        want = run_decode(d, partition_size=P)
+        got = _noalloc(d, P)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (P, wl.name)
+        compare(f64(got), oracle_decode(wl)[0], "bf16", f"noalloc P={P} {wl.name}")
+
+
+def test_noalloc_fp8_long_then_short():
+    """fp8 KV at 512-token partitions: a long batch, then a short one."""
+    long_ = W.decode_workload(seed=302, num_seqs=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              len_lo=20000, len_hi=40000, q_dtype="bf16", kv_dtype="fp8")
+    short = W.decode_workload(seed=303, num_seqs=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              len_lo=1, len_hi=900, q_dtype="bf16", kv_dtype="fp8")
+    for wl in (long_, short):
+        print(f"[noalloc] fp8 {wl.name}: B={wl.num_seqs} tokens={wl.total_tokens}", flush=True)
+        d = Dev(wl)
+        want = run_decode(d, partition_size=512)
+        got = _noalloc(d, 512)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        compare(f64(got), oracle_decode(wl)[0], "fp8", f"noalloc fp8 {wl.name}")
+
+
+def test_noalloc_rejects_a_batch_beyond_the_buffer():
+    """A workspace need above the fixed buffer is refused before anything
+    is enqueued (PA_ERR_WORKSPACE), and the output is left untouched."""
+    import paged_kv_cache_22_amd as pa
+    wl = W.decode_workload(seed=304, num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=100, len_hi=200, q_dtype="bf16", kv_dtype="bf16")
+    d = Dev(wl)
+    # a table 4096 blocks wide, so that the host bound on the lengths may be
+    # 65536 tokens: 4096 partitions of 16 tokens need 135 MB of partials
+    bt = torch.zeros((2, 4096), dtype=torch.int32, device="cuda")
+    bt[:, :d.bt.shape[1]] = d.bt
+    big_len = 16 * bt.shape[1]
+    assert pa.decode_workspace_size(2, 32, 128, big_len, 16) > pa.STATIC_WORKSPACE_BYTES
+    out = torch.zeros_like(d.q)
+    with pytest.raises(pa.PAError, match="PA_ERR_WORKSPACE"):
+        pa.decode_noalloc(d.q, d.k, d.v, bt, d.sl, max_seq_len=big_len, partition_size=16,
+                          out=out)
+    torch.cuda.synchronize()
+    assert (out == 0).all()
