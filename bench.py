@@ -14,12 +14,12 @@ input survives in the L2 or the 256 MB Infinity Cache; a read leaves clean
 lines behind, so no write-back of the flush lands inside the next timed
 kernel.  Step times come from HIP events on the launch stream.
 
-The other workloads (long-context split-KV, the mixed chunked-prefill step,
-fp8 KV, the cache writes that precede attention, and draft verification with
-several queries per sequence) are timed the same way and reported under
-"per_config".  The
-CPU-baseline leg times the fp64 oracle on the host over the whole headline
-batch, repeated for at least 10 s (single thread).
+The other workloads (long-context split-KV, the mixed chunked-prefill step
+timed as one step, fp8 KV, the cache writes that precede attention, and draft
+verification with several queries per sequence) are timed the same way and
+reported under "per_config".  The CPU-baseline leg times the fp64 oracle on
+the host's cores (a process pool over its (sequence, kv-head) pairs) over the
+whole headline batch, repeated for at least 10 s.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
@@ -68,29 +68,84 @@ def stored_traffic(partition_size):
     return int(kv["traffic_bytes_per_launch"])
 
 
+def host_info():
+    """CPU model and core count of the host, ROCm / HIP runtime / driver versions."""
+    info = {"cpu_model": None, "host_cores": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm_version"] = f.read().strip()
+    except OSError:
+        info["rocm_version"] = None
+    try:
+        with open("/sys/module/amdgpu/version") as f:
+            info["amdgpu_driver_version"] = f.read().strip()
+    except OSError:
+        info["amdgpu_driver_version"] = None
+    return info
+
+
+def gpu_info(torch):
+    """Device name, arch and HIP runtime / driver versions (after the GPU is initialised)."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "torch_hip": torch.version.hip}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDriverGetVersion(ctypes.byref(v)) == 0:
+            info["hip_driver_version"] = v.value
+        if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+            info["hip_runtime_version"] = v.value
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(wl, min_seconds=10.0):
-    """The oracle as it stands, single-threaded: the whole batch, repeated
-    until at least min_seconds of CPU work, the mean pass reported."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    passes = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
-                          wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
-            passes += 1
-            total = time.perf_counter() - t0
-            if total >= min_seconds:
-                break
+    """The oracle as it stands, on the host's cores: its (sequence, kv-head)
+    pairs spread over a process pool (one worker per core, at most 16, BLAS
+    at one thread each); the whole batch repeated until at least
+    min_seconds, the mean pass reported.  Started before any GPU use."""
+    from oracle.pool import OraclePool
+    with OraclePool() as pool:
+        args = (wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.scale,
+                wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
+        # inputs written once where the workers map them, and the workers
+        # started: neither is timed
+        staged = pool.stage({"q": wl.q, "k_cache": wl.k_cache, "v_cache": wl.v_cache,
+                             "block_table": wl.block_table, "seq_lens": wl.seq_lens})
+        try:
+            pool.decode(*args, items=[(0, 0)], staged=staged)
+            passes = 0
+            t0 = time.perf_counter()
+            while True:
+                pool.decode(*args, staged=staged)
+                passes += 1
+                total = time.perf_counter() - t0
+                if total >= min_seconds:
+                    break
+        finally:
+            pool.release(staged)
+        workers = pool.workers
     dt = total / passes
-    return {"value": round(wl.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+    info = host_info()
+    return {"value": round(wl.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": workers,
             "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": passes,
             "seconds": round(total, 2),
             "tokens_attended_per_s": round(wl.total_tokens / dt, 1),
+            "cpu_model": info["cpu_model"], "host_cores": info["host_cores"],
             "sample": f"the whole batch ({wl.num_seqs} sequences, {wl.total_tokens} tokens, "
-                      f"all {wl.num_kv_heads} kv-heads), {passes} passes, fp64 numpy oracle, "
-                      f"1 thread"}
+                      f"all {wl.num_kv_heads} kv-heads), {passes} passes, fp64 numpy oracle "
+                      f"over {workers} worker processes (one BLAS thread each), inputs "
+                      f"memory-mapped from one staged copy"}
 
 
 class CacheFlush:
@@ -172,26 +227,84 @@ def time_partition_kernel(torch, pa, d, wl, P, steps, warmup, flush):
     return [t.ms(i, 0, 1) for i in range(steps)]
 
 
-def time_prefill(torch, pa, d, wl, steps, warmup, flush):
-    out = torch.empty_like(d.q)
+def mixed_devices(m):
+    """Device copies of the mixed step: one KV cache shared by its decode rows
+    and its chunks (they are one pool), with each part's own q, tables and
+    lengths."""
+    from workloads.device import Dev
+    dd = Dev(m.decode)
+    dp = Dev.__new__(Dev)
+    dp.wl = m.prefill
+    dp.q = dev_like(m.prefill.q, m.prefill.q_dtype)
+    dp.k, dp.v, dp.ks, dp.vs = dd.k, dd.v, dd.ks, dd.vs
+    dp.bt = dev_like(m.prefill.block_table)
+    dp.sl = dev_like(m.prefill.seq_lens)
+    dp.cu = dev_like(m.prefill.cu_q_lens)
+    return dd, dp
+
+
+def dev_like(arr, tag=None):
+    from workloads.device import dev
+    return dev(arr, tag)
+
+
+def time_mixed(torch, pa, dd, dp, m, P, steps, warmup, flush):
+    """The mixed step as one step: after one cache flush, pa_decode on the
+    decode rows and pa_prefill_chunk on the chunks, back to back on one
+    stream, between one pair of events (a third event between the two gives
+    the split).  Returns per-step (step, decode part, prefill part) ms."""
+    dec, pre = m.decode, m.prefill
+    out_d = torch.empty_like(dd.q)
+    out_p = torch.empty_like(dp.q)
+    ws = torch.empty(max(pa.decode_workspace_size(dec.num_seqs, dec.num_q_heads, dec.head_dim,
+                                                  dec.max_seq_len, P), 256),
+                     dtype=torch.uint8, device="cuda")
 
     def launch(ev):
         ev[0].record()
-        pa.prefill_chunk(d.q, d.cu, d.k, d.v, d.bt, d.sl, max_q_len=wl.max_q_len, scale=wl.scale,
-                         out=out)
+        pa.decode(dd.q, dd.k, dd.v, dd.bt, dd.sl, max_seq_len=dec.max_seq_len, scale=dec.scale,
+                  partition_size=P, out=out_d, workspace=ws)
         ev[1].record()
+        pa.prefill_chunk(dp.q, dp.cu, dp.k, dp.v, dp.bt, dp.sl, max_q_len=pre.max_q_len,
+                         scale=pre.scale, out=out_p)
+        ev[2].record()
 
-    wt = Timer(torch, warmup, 2)
+    wt = Timer(torch, warmup, 3)
     for i in range(warmup):
         flush()
         launch(wt.ev[i])
     torch.cuda.synchronize()
-    t = Timer(torch, steps, 2)
+    t = Timer(torch, steps, 3)
     for i in range(steps):
         flush()
         launch(t.ev[i])
     torch.cuda.synchronize()
-    return [t.ms(i, 0, 1) for i in range(steps)]
+    return ([t.ms(i, 0, 2) for i in range(steps)], [t.ms(i, 0, 1) for i in range(steps)],
+            [t.ms(i, 1, 2) for i in range(steps)])
+
+
+def mixed_summary(m, P, step, dec, pre):
+    mean = lambda xs: sum(xs) / len(xs)
+    sm, dm, pm = mean(step), mean(dec), mean(pre)
+    tflops = m.prefill.flops() / pm / 1e9
+    attended = m.decode.total_tokens + m.prefill.pairs()
+    return {
+        "workload": "mixed step: 16 decode seqs (1024-8192) + 4 chunks of 512 over a 2048-token "
+                    "shared prefix, 32/8 heads, d=128, bf16, seed 4",
+        "decode_partition_size": P,
+        "step_ms": round(sm, 5),
+        "p10_ms": round(sorted(step)[len(step) // 10], 5),
+        "p90_ms": round(sorted(step)[(9 * len(step)) // 10], 5),
+        "tokens_attended_per_s": round(attended / sm * 1e3, 1),
+        "note": "one flush, then pa_decode and pa_prefill_chunk back to back on one stream "
+                "between one pair of HIP events; the parts split at an event between them",
+        "decode": {"ms": round(dm, 5), "kv_bytes": m.decode.kv_bytes(),
+                   "kv_GBps": round(m.decode.kv_bytes() / dm / 1e6, 2),
+                   "pct_hbm_peak": round(100 * m.decode.kv_bytes() / dm / 1e6 / HBM_PEAK_GBS, 2)},
+        "prefill": {"ms": round(pm, 5), "TFLOPs": round(tflops, 2),
+                    "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+                    "pairs": m.prefill.pairs(), "flops": m.prefill.flops()},
+    }
 
 
 def time_verify(torch, pa, W, steps, warmup, flush, partition_size):
@@ -440,14 +553,10 @@ def profile_one(args, W):
     res = {"workload": W.CONFIG_NAMES[n]}
     if n == 4:
         m = W.config4(pad=0, partition_size=args.partition_size)
-        dd, dp = Dev(m.decode), Dev(m.prefill)
-        s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, args.steps,
-                           args.warmup, flush)
-        pms = time_prefill(torch, pa, dp, m.prefill, args.steps, args.warmup, flush)
-        pre_ms = sum(pms) / len(pms)
-        res["decode"] = decode_summary(m.decode, s, k)
-        res["prefill_ms"] = round(pre_ms, 5)
-        res["prefill_TFLOPs"] = round(m.prefill.flops() / pre_ms / 1e9, 2)
+        dd, dp = mixed_devices(m)
+        step, dec, pre = time_mixed(torch, pa, dd, dp, m, args.partition_size, args.steps,
+                                    args.warmup, flush)
+        res.update(mixed_summary(m, args.partition_size, step, dec, pre))
     else:
         w = W.config3(pad=0) if n == 3 else W.config5(pad=0, partition_size=args.partition_size)
         dd = Dev(w)
@@ -524,24 +633,11 @@ def main():
             per_config[w.name]["balanced"] = {kk: vv for kk, vv in decode_summary(w, s, k).items()
                                               if kk in ("ms_per_step", "kv_GBps", "pct_hbm_peak")}
             del dd
-        # the mixed step's decode rows (16 long sequences) balanced across the chip
+        # the mixed step, timed as one step (decode rows balanced across the chip)
         m = W.config4(pad=0, partition_size=-1)
-        dd, dp = Dev(m.decode), Dev(m.prefill)
-        s, k = time_decode(torch, pa, dd, m.decode, m.decode.partition_size, 20, 3, flush)
-        pms = time_prefill(torch, pa, dp, m.prefill, 20, 3, flush)
-        pre_ms = sum(pms) / len(pms)
-        dec = decode_summary(m.decode, s, k)
-        dec["partition_size"] = m.decode.partition_size
-        tflops = m.prefill.flops() / pre_ms / 1e9
-        per_config["C4"] = {
-            "workload": W.CONFIG_NAMES[4],
-            "step_ms": round(dec["ms_per_step"] + pre_ms, 5),
-            "decode": dec,
-            "prefill": {"ms": round(pre_ms, 5), "TFLOPs": round(tflops, 2),
-                        "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
-                        "pairs": m.prefill.pairs(), "flops": m.prefill.flops(),
-                        "tokens_attended_per_s": round(m.prefill.pairs() / pre_ms * 1e3, 1)},
-        }
+        dd, dp = mixed_devices(m)
+        step, dec, pre = time_mixed(torch, pa, dd, dp, m, -1, 20, 3, flush)
+        per_config["C4"] = mixed_summary(m, -1, step, dec, pre)
         del dd, dp
         per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
         per_config["verify"] = time_verify(torch, pa, W, 20, 3, flush, args.partition_size)
@@ -592,6 +688,7 @@ def main():
                     "mode changed since",
         },
         "cpu_baseline": cpu,
+        "host": {**host_info(), **gpu_info(torch)},
         "per_config": per_config,
     }
     print(json.dumps(line), flush=True)

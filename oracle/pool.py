@@ -8,14 +8,15 @@ No arithmetic lives here.  Decode attention of one (sequence, kv-head) pair
 and causal prefill of one (chunk, kv-head) pair are independent of every
 other pair, so each worker process calls the oracle's own per-pair functions
 (``decode_rows``, ``prefill_rows``) and the parent only places the returned
-rows.  The result is bit-identical to the single-process oracle.
+rows.  The result is bit-identical to the single-process oracle's.
 
 Workers are started with the "spawn" method (fresh interpreters that import
 numpy and this package only; they never touch a GPU), each with its BLAS
 pinned to one thread.  The input arrays -- caches of several GB at the long
 context -- are written once per call as ``.npy`` files into a temporary
 directory (``/dev/shm`` when it has room) and memory-mapped read-only by the
-workers, so no worker holds a private copy.
+workers, so no worker holds a private copy; a worker keeps the maps of the
+directory it last read.
 """
 from __future__ import annotations
 
@@ -55,13 +56,21 @@ def _init_worker():
         pass
 
 
+_OPENED = {"key": None, "arrays": None}
+
+
 def _open(dirpath: str):
-    arrs = {}
-    for n in _NAMES:
-        f = os.path.join(dirpath, n + ".npy")
-        if os.path.exists(f):
-            arrs[n] = np.load(f, mmap_mode="r")
-    return arrs
+    """The staged arrays of ``dirpath`` as read-only ndarrays over the mapped
+    files; the last directory's maps are kept for the tasks that follow."""
+    key = (dirpath, os.stat(os.path.join(dirpath, "q.npy")).st_mtime_ns)
+    if _OPENED["key"] != key:
+        arrs = {}
+        for n in _NAMES:
+            f = os.path.join(dirpath, n + ".npy")
+            if os.path.exists(f):
+                arrs[n] = np.asarray(np.load(f, mmap_mode="r"))
+        _OPENED["key"], _OPENED["arrays"] = key, arrs
+    return _OPENED["arrays"]
 
 
 def _decode_task(task):
@@ -119,7 +128,10 @@ class OraclePool:
 
     # -- shared inputs -------------------------------------------------------
     @staticmethod
-    def _stage(arrays: dict) -> str:
+    def stage(arrays: dict) -> str:
+        """Write the named input arrays where the workers map them; returns
+        the directory, to pass as ``staged`` to calls on the same inputs and
+        to ``release`` afterwards."""
         need = sum(a.nbytes for a in arrays.values() if a is not None)
         base = None
         try:
@@ -134,14 +146,19 @@ class OraclePool:
                 np.save(os.path.join(d, n + ".npy"), np.ascontiguousarray(a))
         return d
 
+    @staticmethod
+    def release(dirpath: str) -> None:
+        shutil.rmtree(dirpath, ignore_errors=True)
+
     def _run(self, fn, tasks: Sequence[tuple]):
         return list(self._pool.imap_unordered(fn, tasks, chunksize=1))
 
     # -- the oracle's entry points -------------------------------------------
     def decode(self, q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: str,
                kv_dtype: str, k_scale=None, v_scale=None,
-               items: Optional[Iterable[Tuple[int, int]]] = None):
-        """oracle.decode, its (sequence, kv-head) pairs spread over the workers."""
+               items: Optional[Iterable[Tuple[int, int]]] = None, staged: Optional[str] = None):
+        """oracle.decode, its (sequence, kv-head) pairs spread over the workers.
+        ``staged``: a directory from ``stage`` holding these same inputs."""
         B, Hq, d = q.shape
         Hkv = k_cache.shape[1]
         G = Hq // Hkv
@@ -152,15 +169,16 @@ class OraclePool:
         vs = None if v_scale is None else np.asarray(v_scale, np.float32).copy()
         out = np.full((B, Hq, d), np.nan)
         lse = np.full((B, Hq), np.nan)
-        dirpath = self._stage({"q": q, "k_cache": k_cache, "v_cache": v_cache,
-                               "block_table": block_table, "seq_lens": seq_lens})
+        dirpath = staged or self.stage({"q": q, "k_cache": k_cache, "v_cache": v_cache,
+                                        "block_table": block_table, "seq_lens": seq_lens})
         try:
             tasks = [(dirpath, scale, q_dtype, kv_dtype, ks, vs, int(b), int(h)) for b, h in todo]
             for b, h, o, l in self._run(_decode_task, tasks):
                 out[b, h * G:(h + 1) * G] = o
                 lse[b, h * G:(h + 1) * G] = l
         finally:
-            shutil.rmtree(dirpath, ignore_errors=True)
+            if staged is None:
+                self.release(dirpath)
         return out, lse
 
     def prefill_chunk(self, q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: float,
@@ -177,7 +195,7 @@ class OraclePool:
         vs = None if v_scale is None else np.asarray(v_scale, np.float32).copy()
         out = np.full((total_q, Hq, d), np.nan)
         lse = np.full((total_q, Hq), np.nan)
-        dirpath = self._stage({"q": q, "cu_q_lens": cu_q_lens, "k_cache": k_cache,
+        dirpath = self.stage({"q": q, "cu_q_lens": cu_q_lens, "k_cache": k_cache,
                                "v_cache": v_cache, "block_table": block_table,
                                "seq_lens": seq_lens})
         try:
@@ -187,7 +205,7 @@ class OraclePool:
                 out[q0:q1, h * G:(h + 1) * G] = o
                 lse[q0:q1, h * G:(h + 1) * G] = l
         finally:
-            shutil.rmtree(dirpath, ignore_errors=True)
+            self.release(dirpath)
         return out, lse
 
 
