@@ -23,6 +23,15 @@
  *                      tile is a run of 16-byte chunks of consecutive dims, with the
  *                      token index inside each chunk
  *   v_cache            [num_blocks, num_kv_heads, head_dim, block_size]  (dim-major tiles)
+ *                      The pages leave the cache layout to the platform (vllm-metal
+ *                      architecture article, section 二).  These two differ from plain
+ *                      token-major rows [num_blocks, num_kv_heads, block_size, head_dim]
+ *                      on purpose: the score product contracts over dims, and with the
+ *                      chunked K tile one load instruction of a wave reads 1 KiB in one
+ *                      piece (16 half-lines with token-major rows; the bf16 Llama-3-8B
+ *                      decode went from 58% to 67% of peak bandwidth with the change);
+ *                      the output product contracts over tokens, which the dim-major V
+ *                      tile serves with whole dim rows.
  *   block_table        int32 [num_seqs, max_blocks_per_seq]; logical token t of
  *                      sequence b lives in physical block block_table[b][t / block_size]
  *                      at slot t % block_size
@@ -41,13 +50,20 @@
  * (BF16, FP8_E4M3); out has q's dtype; q, out, k_cache, v_cache 16-byte
  * aligned.
  *
- * Ownership and execution.  The library owns no memory and keeps no state
- * between calls.  Every call only validates its scalar arguments and pointer
- * alignment on the host and enqueues kernels on `stream` (a hipStream_t;
- * NULL = the default stream).  It never reads device memory from the host,
- * never synchronises and never allocates, so calls can be captured in a HIP
- * graph.  Table entries at or past ceil(seq_len / block_size) and cache
- * slots past seq_len are never read (they may hold anything, NaN included).
+ * Ownership and execution.  The caller owns every buffer passed in.  Every
+ * call only validates its scalar arguments and pointer alignment on the host
+ * and enqueues kernels on `stream` (a hipStream_t; NULL = the default
+ * stream).  It never reads device memory from the host, never synchronises
+ * and never allocates, so calls can be captured in a HIP graph (the kernels
+ * join the caller's step with no sync boundary, as the vllm-metal
+ * architecture article, section 三, asks of its native kernels).  Host
+ * state, kept per device for the life of the process: the number of
+ * workgroups of the balanced decode mode the device holds at once (one
+ * occupancy query on the first balanced call) and the address of
+ * pa_decode_noalloc's fixed buffer (looked up on its first call).  Make
+ * those first calls outside graph capture.  Table entries at or past
+ * ceil(seq_len / block_size) and cache slots past seq_len are never read
+ * (they may hold anything, NaN included).
  *
  * Errors.  A non-zero pa_status is returned before anything is enqueued when
  * the arguments are invalid.  A call with nothing to do (num_seqs == 0,
@@ -113,7 +129,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
 
 /*
  * Decode attention: one query per sequence (the newest token, already in the
- * cache) attends to keys 0 .. seq_lens[b]-1.
+ * cache) attends to keys 0 .. seq_lens[b]-1.  The pages name this step: the
+ * native paged-attention kernel driven by block tables and sequence lengths
+ * that stay device tensors (vllm-metal architecture article, sections 三
+ * and 四), with GQA 4:1 and FP8 KV at scale amax / 448 (vllm-metis 0.1.0,
+ * "Status"); the split of long contexts into partitions merged by their
+ * log-sum-exp is this library's (the pages give no rule for it).
  *
  * partition_size == 0: one pass per (sequence, kv-head), out written
  * directly.  partition_size > 0 (a multiple of 16 tokens): split-KV; each
@@ -135,6 +156,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * sequence a range covers costs it a table load and a first-block load in
  * series, so for large batches of short sequences (hundreds to thousands
  * of sequences of a few hundred tokens) the one-pass mode is faster.
+ * Batch invariance: where a sequence's pieces begin depends on the whole
+ * batch's blocks and on the device's occupancy, so in the balanced mode a
+ * sequence's output bits can change with its batch-mates and with the GPU
+ * model (within the merge's rounding: one bf16 step).  The one-pass mode and
+ * fixed partitions are batch-invariant bit for bit: a sequence's result
+ * depends only on its own inputs (the pages name batch-dependent outputs as
+ * a limitation of per-batch FP8 scales: vllm-metis 0.1.0, "Limitations").
  * max_seq_len is the caller's host-side
  * bound on seq_lens; it sizes the grid.  A sequence of length 0 gets zeros.
  * scale is the softmax scale (1/sqrt(head_dim) for plain attention); it
@@ -271,7 +299,10 @@ int pa_decode_partitions(float* partial_out, float* partial_lse, int max_partiti
                          void* stream);
 
 /*
- * Log-sum-exp merge of split-KV partials.  For sequence b only partitions
+ * Log-sum-exp merge of split-KV partials (the standard combination of
+ * softmax pieces over disjoint key sets; the pages give no merge rule, and
+ * the exactness of the combination is what the oracle's split = unsplit pin
+ * checks).  For sequence b only partitions
  * p < ceil(seq_lens[b] / partition_size) take part:
  *     M = max_p lse_p,  w_p = exp(lse_p - M),
  *     out = sum_p w_p o_p / sum_p w_p,  out_lse = M + ln sum_p w_p.
@@ -284,7 +315,10 @@ int pa_merge_partitions(void* out, int out_dtype, float* out_lse,
                         int num_seqs, int num_q_heads, int head_dim, void* stream);
 
 /*
- * Causal chunked prefill over a paged context.  Chunk c owns query rows
+ * Causal chunked prefill over a paged context: chunked prefill and prefix
+ * caching are how the pages' serving engine runs long prompts (vllm-metis
+ * 0.1.0, "How the model maps onto vLLM"; its "Status" reports parity with
+ * 64-token chunks and prefix-cache hits).  Chunk c owns query rows
  * cu_q_lens[c] .. cu_q_lens[c+1]-1 of `q`; its sequence has seq_lens[c]
  * tokens in the cache (the context followed by the chunk itself), so with
  * ctx = seq_lens[c] - q_len_c, query i of the chunk sits at position ctx + i
@@ -330,6 +364,12 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
  *                  code); k_scale and v_scale must be finite and > 0.
  * Slots not named by slot_mapping are left untouched.  With num_tokens == 0
  * nothing is launched, and key, value and slot_mapping may be NULL.
+ * Cost: a whole 16-token group written into one block moves its rows at
+ * copy speed; a single new token per sequence (a decode step) writes each
+ * V element into its own dim row of the dim-major tile, so the memory
+ * system writes whole 32-byte sectors for 2-byte elements (measured: about
+ * 9x the row bytes for a 64-sequence bf16 decode step, 2.4 MB for 0.26 MB;
+ * small beside the step's attention reads).
  */
 int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype,
                 const void* key, const void* value, int in_dtype,
