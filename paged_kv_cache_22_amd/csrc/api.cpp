@@ -113,20 +113,21 @@ constexpr int kPrefixWGs = PA_PREFIX_WGS;
 
 // tokens per key range (a multiple of 32): about kPrefixWGs / (row groups x
 // kv-heads) ranges over the prefix
-int prefix_key_range(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int prefix_len) {
+long long prefix_key_range(int num_seqs, int q_len, int num_q_heads, int num_kv_heads,
+                           int prefix_len) {
     const long long rows = (long long)num_seqs * q_len * (num_q_heads / num_kv_heads);
     const long long groups = (rows + 127) / 128 * num_kv_heads;   // 128 rows per workgroup
-    long long want = (kPrefixWGs + groups - 1) / groups;
+    long long want = groups > 0 ? (kPrefixWGs + groups - 1) / groups : 1;
     if (want < 1) want = 1;
-    const long long per = (prefix_len + want - 1) / want;
-    return (int)((per + 31) / 32 * 32);
+    const long long per = ((long long)prefix_len + want - 1) / want;
+    return (per + 31) / 32 * 32;
 }
 
 // the ranges that key range actually makes (every one holds keys)
 int prefix_ranges(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int prefix_len) {
     if (prefix_len <= 0) return 0;
-    const int kr = prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
-    return (prefix_len + kr - 1) / kr;
+    const long long kr = prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
+    return (int)(((long long)prefix_len + kr - 1) / kr);
 }
 
 }  // namespace
@@ -153,6 +154,10 @@ int pa_version(void) { return 100; }
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
                                 int partition_size) {
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return 0;
+    // sizes the calls themselves refuse have no workspace size
+    if ((long long)num_seqs * num_q_heads > 0x7fffffffLL) return 0;
+    if (partition_size > 0 && ((long long)max_seq_len + partition_size - 1) / partition_size > kMaxGridY)
+        return 0;
     if (partition_size == PA_PARTITION_BALANCED) {
         // piece records | partial outputs | partial lse, for up to
         // kMaxBalancedSplits splits per kv-head
@@ -451,6 +456,12 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int q_len, int num_q
     if (num_seqs < 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         prefix_len < 0 || max_seq_len < 0 || partition_size <= 0)
         return 0;
+    // sizes the call itself refuses have no workspace size
+    if (num_q_heads % num_kv_heads != 0) return 0;
+    if ((long long)num_seqs * q_len > 0x7fffffffLL ||
+        (long long)num_seqs * q_len * num_q_heads > 0x7fffffffLL)
+        return 0;
+    if (((long long)max_seq_len + partition_size - 1) / partition_size > kMaxGridY) return 0;
     const size_t slots = (size_t)prefix_ranges(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len) +
                          ((size_t)max_seq_len + partition_size - 1) / partition_size;
     const size_t rows = (size_t)num_seqs * q_len * num_q_heads * slots;
@@ -466,7 +477,7 @@ int pa_decode_shared_prefix(void* out, const void* q, int q_dtype, int q_len, co
                             float scale, const float* k_scale, const float* v_scale,
                             int partition_size, int max_seq_len, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    if (q_len <= 0 || prefix_len < 0) return PA_ERR_SHAPE;
+    if (q_len <= 0 || prefix_len < 0 || prefix_len > 0x7fffffff - 64) return PA_ERR_SHAPE;
     if (partition_size <= 0) return PA_ERR_UNSUPPORTED;
     int st = decode_checks(q, q_dtype, k_cache, v_cache, kv_dtype, block_table, max_blocks_per_seq,
                            seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -520,7 +531,7 @@ int pa_decode_shared_prefix(void* out, const void* q, int q_dtype, int q_len, co
     p.block_size = block_size;
     p.scale = scale;
     p.kv_len = prefix_len;
-    p.key_range = prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
+    p.key_range = (int)prefix_key_range(num_seqs, q_len, num_q_heads, num_kv_heads, prefix_len);
     p.part_out = part_out;
     p.part_lse = part_lse;
     p.part_stride = slots;
