@@ -18,11 +18,14 @@
  * Memory layouts (row-major, contiguous, all device memory):
  *   q, out (decode)    [num_seqs, num_q_heads, head_dim]
  *   q, out (prefill)   [total_q,  num_q_heads, head_dim]
- *   k_cache            [num_blocks, num_kv_heads, head_dim / X, block_size, X], X the
- *                      dims in 16 bytes (4 fp32, 8 bf16, 16 fp8): each (block, kv-head)
+ *   k_cache            [num_blocks, n, num_kv_heads, head_dim / X, 16, X], n = block_size
+ *                      / 16, X the dims in 16 bytes (4 fp32, 8 bf16, 16 fp8): a block is
+ *                      n consecutive 16-token sub-blocks, and each (sub-block, kv-head)
  *                      tile is a run of 16-byte chunks of consecutive dims, with the
- *                      token index inside each chunk
- *   v_cache            [num_blocks, num_kv_heads, head_dim, block_size]  (dim-major tiles)
+ *                      token index inside each chunk.  Token slot s of a block is slot
+ *                      s % 16 of sub-block s / 16; with 16-token blocks (n = 1) this is
+ *                      [num_blocks, num_kv_heads, head_dim / X, 16, X].
+ *   v_cache            [num_blocks, n, num_kv_heads, head_dim, 16]  (dim-major tiles)
  *                      The pages leave the cache layout to the platform (vllm-metal
  *                      architecture article, section 二).  These two differ from plain
  *                      token-major rows [num_blocks, num_kv_heads, block_size, head_dim]
@@ -31,7 +34,14 @@
  *                      piece (16 half-lines with token-major rows; the bf16 Llama-3-8B
  *                      decode went from 58% to 67% of peak bandwidth with the change);
  *                      the output product contracts over tokens, which the dim-major V
- *                      tile serves with whole dim rows.
+ *                      tile serves with whole dim rows.  Splitting 32- and 64-token
+ *                      blocks into 16-token sub-blocks keeps every V load a whole run of
+ *                      16-token rows (with [.., head_dim, block_size] V tiles a load
+ *                      covered 32-byte slices of 64- or 128-byte rows: 64-token blocks
+ *                      measured 61% of peak bandwidth, 74% with sub-blocks).  The cache
+ *                      of num_blocks blocks is byte for byte a cache of num_blocks * n
+ *                      16-token blocks; slot numbers (block * block_size + offset) are
+ *                      the same in both readings.
  *   block_table        int32 [num_seqs, max_blocks_per_seq]; logical token t of
  *                      sequence b lives in physical block block_table[b][t / block_size]
  *                      at slot t % block_size

@@ -26,9 +26,11 @@ this oracle writes out the plain definition of each step:
   out = sum_p w_p o_p / sum_p w_p with w_p = exp(lse_p - max lse);
 * FP8 KV: value = e4m3fn(code) * scale[kv_head], per K and per V.
 
-Layouts (see ``k_block`` / ``v_block``, the only two places that know them):
-k_cache[num_blocks, Hkv, d/X, block_size, X] (X dims per chunk),
-v_cache[num_blocks, Hkv, d, block_size].
+Layouts (see ``k_block`` / ``v_block``, the only places that read them, and
+``write_kv``): a block of bs tokens is n = bs / 16 consecutive 16-token
+sub-blocks, k_cache[num_blocks, n, Hkv, d/X, 16, X] (X dims per chunk) and
+v_cache[num_blocks, n, Hkv, d, 16]; with 16-token blocks the n axis is left
+out, k_cache[num_blocks, Hkv, d/X, 16, X] and v_cache[num_blocks, Hkv, d, 16].
 Storage dtypes: "f32" float32, "bf16" uint16 bit patterns, "fp8" uint8 codes.
 """
 from __future__ import annotations
@@ -61,19 +63,35 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # the block-table walk
 # ---------------------------------------------------------------------------
+def block_size(v_cache) -> int:
+    """Tokens per cache block: 16 times the sub-blocks per block."""
+    return 16 if v_cache.ndim == 4 else 16 * v_cache.shape[1]
+
+
+def kv_heads(k_cache) -> int:
+    """kv-heads of a K cache (the axis after the block, or after the sub-block)."""
+    return k_cache.shape[1] if k_cache.ndim == 5 else k_cache.shape[2]
+
+
 def k_block(k_cache, phys: int, h: int, n: int) -> np.ndarray:
     """Keys of slots 0..n-1 of (physical block, kv-head), as rows [n, d].
 
-    The K tile is stored as [d / X][block_size][X]: chunks of X consecutive
-    dims, the slot index inside a chunk (X is the array's last extent)."""
-    tile = k_cache[phys, h, :, :n, :]                  # [d/X, n, X]
-    return tile.transpose(1, 0, 2).reshape(n, -1)
+    Slot t is slot t mod 16 of sub-block t // 16.  A sub-block's K tile is
+    stored as [d / X][16][X]: chunks of X consecutive dims, the slot index
+    inside a chunk (X is the array's last extent)."""
+    ns = -(-n // 16)
+    tiles = k_cache[phys:phys + 1, h] if k_cache.ndim == 5 else k_cache[phys, :ns, h]
+    rows = tiles.transpose(0, 2, 1, 3)                 # [sub-block, slot, d/X, X]
+    return rows.reshape(-1, rows.shape[2] * rows.shape[3])[:n]
 
 
 def v_block(v_cache, phys: int, h: int, n: int) -> np.ndarray:
     """Values of slots 0..n-1 of (physical block, kv-head), as rows [n, d]:
-    the V tile is stored dim-major, so its first n columns are read."""
-    return v_cache[phys, h, :, :n].T
+    each sub-block's V tile is stored dim-major [d][16]."""
+    ns = -(-n // 16)
+    tiles = v_cache[phys:phys + 1, h] if v_cache.ndim == 4 else v_cache[phys, :ns, h]
+    rows = tiles.transpose(0, 2, 1)                    # [sub-block, slot, d]
+    return rows.reshape(-1, rows.shape[2])[:n]
 
 
 def gather_kv(k_cache, v_cache, table_row, seq_len: int, h: int, kv_dtype: str,
@@ -85,8 +103,8 @@ def gather_kv(k_cache, v_cache, table_row, seq_len: int, h: int, kv_dtype: str,
     the last block.  Returns float64 K [L, d] and V [L, d] (fp8 values
     multiplied by the head's scale).
     """
-    bs = v_cache.shape[3]
-    d = v_cache.shape[2]
+    bs = block_size(v_cache)
+    d = v_cache.shape[-2]
     K = np.empty((seq_len, d), dtype=np.float64)
     V = np.empty((seq_len, d), dtype=np.float64)
     for j in range(-(-seq_len // bs)):
@@ -129,7 +147,7 @@ def decode_rows(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtyp
     h*G .. h*G+G-1 of sequence b against its keys 0 .. L-1.  Returns
     (out[G, d], lse[G]) in float64."""
     Hq = q.shape[1]
-    G = _heads(Hq, k_cache.shape[1])
+    G = _heads(Hq, kv_heads(k_cache))
     qf = widen(q[b, h * G:(h + 1) * G], q_dtype)
     K, V = gather_kv(k_cache, v_cache, block_table[b], int(seq_lens[b]), h, kv_dtype,
                      k_scale, v_scale)
@@ -149,7 +167,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_dtype: st
     are left NaN so that a caller cannot mistake them for results.
     """
     B, Hq, d = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = kv_heads(k_cache)
     G = _heads(Hq, Hkv)
     out = np.full((B, Hq, d), np.nan)
     lse = np.full((B, Hq), np.nan)
@@ -170,7 +188,7 @@ def decode_partials(q, k_cache, v_cache, block_table, seq_lens, scale: float, q_
     token have o = 0 and lse = -inf.
     """
     B, Hq, d = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = kv_heads(k_cache)
     G = _heads(Hq, Hkv)
     P = partition_size
     qf = widen(q, q_dtype)
@@ -219,7 +237,7 @@ def prefill_rows(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: f
     (ctx = seq_lens[c] - n) and sees keys 0 .. ctx + i.  Returns
     (out[n, G, d], lse[n, G]) in float64."""
     Hq, d = q.shape[1], q.shape[2]
-    G = _heads(Hq, k_cache.shape[1])
+    G = _heads(Hq, kv_heads(k_cache))
     q0, q1 = int(cu_q_lens[c]), int(cu_q_lens[c + 1])
     L = int(seq_lens[c])
     ctx = L - (q1 - q0)
@@ -247,7 +265,7 @@ def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, scale: 
     ``items`` restricts the work to (chunk, kv-head) pairs (others stay NaN).
     """
     total_q, Hq, d = q.shape
-    Hkv = k_cache.shape[1]
+    Hkv = kv_heads(k_cache)
     G = _heads(Hq, Hkv)
     out = np.full((total_q, Hq, d), np.nan)
     lse = np.full((total_q, Hq), np.nan)
@@ -294,14 +312,15 @@ def write_kv(k_cache, v_cache, key, value, slot_mapping, in_dtype: str, kv_dtype
     nearest even with saturation at 448 (the amax / 448 scale rule of
     vllm-metis 0.1.0, "Status", applied on write).
     """
-    bs = v_cache.shape[3]
+    bs = block_size(v_cache)
     T, Hkv, d = key.shape
-    kx = k_cache.shape[4]
+    kx = k_cache.shape[-1]
     for t in range(T):
         s = int(slot_mapping[t])
         if s < 0:
             continue
         phys, off = s // bs, s % bs
+        sub, o = off // 16, off % 16
         for h in range(Hkv):
             kr, vr = key[t, h], value[t, h]
             if kv_dtype == "fp8":
@@ -311,6 +330,8 @@ def write_kv(k_cache, v_cache, key, value, slot_mapping, in_dtype: str, kv_dtype
                 kq, vq = kr, vr
             else:
                 raise ValueError("a bf16 / fp32 cache takes inputs of its own type")
-            k_cache[phys, h, :, off, :] = np.asarray(kq).reshape(d // kx, kx)
-            v_cache[phys, h, :, off] = vq
+            kt = k_cache[phys, h] if k_cache.ndim == 5 else k_cache[phys, sub, h]
+            vt = v_cache[phys, h] if v_cache.ndim == 4 else v_cache[phys, sub, h]
+            kt[:, o, :] = np.asarray(kq).reshape(d // kx, kx)
+            vt[:, o] = vq
     return k_cache, v_cache

@@ -160,7 +160,7 @@ class OraclePool:
         """oracle.decode, its (sequence, kv-head) pairs spread over the workers.
         ``staged``: a directory from ``stage`` holding these same inputs."""
         B, Hq, d = q.shape
-        Hkv = k_cache.shape[1]
+        Hkv = attention.kv_heads(k_cache)
         G = Hq // Hkv
         todo = list(items) if items is not None else [(b, h) for b in range(B) for h in range(Hkv)]
         # longest sequences first, so no worker is left with a long one at the end
@@ -186,7 +186,7 @@ class OraclePool:
                       items: Optional[Iterable[Tuple[int, int]]] = None):
         """oracle.prefill_chunk, its (chunk, kv-head) pairs spread over the workers."""
         total_q, Hq, d = q.shape
-        Hkv = k_cache.shape[1]
+        Hkv = attention.kv_heads(k_cache)
         G = Hq // Hkv
         n_chunks = len(seq_lens)
         todo = list(items) if items is not None else [(c, h) for c in range(n_chunks)

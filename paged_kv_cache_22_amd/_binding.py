@@ -117,18 +117,34 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_se
                                             partition_size))
 
 
-def _kv_dims(q, k_cache, v_cache):
-    """Shapes of q [B, Hq, d], k_cache [NB, Hkv, d/X, bs, X] (X = dims per
-    16 bytes) and v_cache [NB, Hkv, d, bs]."""
-    B, Hq, d = q.shape
-    if k_cache.dim() != 5:
-        raise ValueError("k_cache must be [NB, Hkv, d/X, bs, X] with X = 16 bytes of dims")
-    NB, Hkv, nchunk, bs, x = k_cache.shape
+def _cache_dims(k_cache, v_cache, d):
+    """(NB, Hkv, block size) of a paged cache: a block of bs tokens is
+    n = bs / 16 sub-blocks, k_cache [NB, n, Hkv, d/X, 16, X] (X = dims per
+    16 bytes) and v_cache [NB, n, Hkv, d, 16]; 16-token blocks may leave the
+    n axis out."""
+    if k_cache.dim() == 5:
+        NB, Hkv, nchunk, t, x = k_cache.shape
+        n = 1
+        vshape = (NB, Hkv, d, 16)
+    elif k_cache.dim() == 6:
+        NB, n, Hkv, nchunk, t, x = k_cache.shape
+        vshape = (NB, n, Hkv, d, 16)
+    else:
+        raise ValueError("k_cache must be [NB, n, Hkv, d/X, 16, X] (or [NB, Hkv, d/X, 16, X])")
+    if t != 16 or n not in (1, 2, 4):
+        raise ValueError("the cache holds 16-token sub-blocks, 1, 2 or 4 per block")
     if x * k_cache.element_size() != 16 or nchunk * x != d:
         raise ValueError(f"k_cache chunks must hold 16 bytes ({16 // k_cache.element_size()} "
                          f"dims) and cover head_dim {d}")
-    if tuple(v_cache.shape) != (NB, Hkv, d, bs):
-        raise ValueError("v_cache must be [NB, Hkv, d, bs]")
+    if tuple(v_cache.shape) != vshape:
+        raise ValueError(f"v_cache must be {list(vshape)}")
+    return NB, Hkv, 16 * n
+
+
+def _kv_dims(q, k_cache, v_cache):
+    """Shapes of q [B, Hq, d] and the paged cache."""
+    B, Hq, d = q.shape
+    NB, Hkv, bs = _cache_dims(k_cache, v_cache, d)
     return B, Hq, d, NB, Hkv, bs
 
 
@@ -358,11 +374,9 @@ def write_kv(key, value, k_cache, v_cache, slot_mapping, *, k_scale=None, v_scal
     T, Hkv, d = key.shape
     if tuple(value.shape) != (T, Hkv, d):
         raise ValueError("value must have key's shape")
-    NB, Hkv_c, nchunk, bs, x = k_cache.shape
-    if Hkv_c != Hkv or nchunk * x != d or x * k_cache.element_size() != 16:
-        raise ValueError("k_cache must be [NB, Hkv, d/X, bs, X] matching key")
-    if tuple(v_cache.shape) != (NB, Hkv, d, bs):
-        raise ValueError("v_cache must be [NB, Hkv, d, bs]")
+    NB, Hkv_c, bs = _cache_dims(k_cache, v_cache, d)
+    if Hkv_c != Hkv:
+        raise ValueError("the cache's kv-heads must match key's")
     if slot_mapping.dim() != 1 or slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping must be [T]")
     kp, ks_ = _rows(key, "key")

@@ -61,8 +61,8 @@ struct RangeOut {
 template <int D, int KIND, int BS, bool MQ, int WAVES>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, int L, int j0, int j1,
                                              const RangeOut& dst, float* smem) {
-    using T = Tile<KIND, D, BS>;
-    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
+    using T = Tile<KIND, D>;
+    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(sub-blocks per block)
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
 
@@ -95,7 +95,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
 
     // block-table window of this wave: lane i holds the table entry of its
     // unit number tbase + i (and tbase + 64 + i in tnxt); unit u of the
-    // sequence lies in block u / (BS / 16)
+    // sequence is sub-block u mod (BS / 16) of block u / (BS / 16)
     const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq;
     const int ubase = j0 + w;  // the wave's unit i is ubase + i * WAVES
     int tbase = 0;
@@ -104,15 +104,15 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
 
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
-    const size_t blk_stride = (size_t)Hkv * T::kTileBytes;
+    const size_t sub_stride = (size_t)Hkv * T::kTileBytes;   // bytes of one 16-token sub-block
 
     auto issue = [&](typename T::Regs& R, int i) {
         const int idx = i - tbase;
         const int phys = idx < 64 ? __builtin_amdgcn_readlane(tcur, idx)
                                   : __builtin_amdgcn_readlane(tnxt, idx - 64);
-        const size_t off = (size_t)phys * blk_stride;
-        const int sub = (ubase + i * WAVES) & ((1 << kSubShift) - 1);  // unit within the block
-        T::load(R, kbase + off + sub * T::kUnitK, vbase + off + sub * T::kUnitV, r, c);
+        const int sub = (ubase + i * WAVES) & ((1 << kSubShift) - 1);  // sub-block within the block
+        const size_t off = (((size_t)phys << kSubShift) + sub) * sub_stride;
+        T::load(R, kbase + off, vbase + off, r, c);
     };
 
     float m = -INFINITY, l = 0.f;

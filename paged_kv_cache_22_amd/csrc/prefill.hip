@@ -69,11 +69,11 @@ __device__ __forceinline__ void barrier_lds() {
 
 template <int D, int KIND, int BS, int NC>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
-    using T = Tile<KIND, D, BS>;
+    using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
-    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(units per block)
-    constexpr int UB = T::kUnitBytes;                       // one 16-token K (or V) unit
+    constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(sub-blocks per block)
+    constexpr int UB = T::kTileBytes;                       // one 16-token K (or V) tile
     constexpr int kCopies = UB / 1024;                       // 1 KiB copies per unit
     static_assert(UB % 1024 == 0 && kCopies * 4 % kWaves == 0, "whole copies per wave");
     constexpr int kPerWave = kCopies * 4 / kWaves;           // copies per wave and step
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
         (size_t)ch * a.max_blocks_per_seq;
     const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)h * T::kTileBytes;
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)h * T::kTileBytes;
-    // bytes between consecutive physical blocks (a 32-bit quantity: Hkv tiles)
-    const uint32_t blk_stride = (uint32_t)Hkv * (uint32_t)T::kTileBytes;
+    // bytes between consecutive 16-token sub-blocks (a 32-bit quantity: Hkv tiles)
+    const uint32_t sub_stride = (uint32_t)Hkv * (uint32_t)T::kTileBytes;
 
     // Copy k of this wave in a step is copy q = w + kWaves * k of the step's
     // 4 * kCopies: region q / kCopies (K of A, K of B, V of A, V of B), its
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     for (int k = 0; k < kPerWave; ++k) {
         const int q = w + kWaves * k, reg = q / kCopies;
         const int b = (q % kCopies) * 1024 + lane * 16;   // byte of the unit's LDS copy
-        voff[k] = reg < 2 ? (uint32_t)k_lds_hbm<T, BS>(b) : (uint32_t)T::v_slot_hbm(b / 16);
+        voff[k] = reg < 2 ? (uint32_t)k_lds_hbm<T>(b) : (uint32_t)T::v_slot_hbm(b / 16);
     }
     const int nsteps = (nblk - ubeg + 1) / 2;
     // the physical blocks of step t's units (a missing second unit re-reads
@@ -197,15 +197,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     auto copy_step = [&](int t, int pa, int pb) {
         const int ja = ubeg + 2 * t, jb = min(ja + 1, nblk - 1);
         char* st = stage[t % kStages];
-        const uint64_t oa = (uint64_t)(uint32_t)pa * blk_stride;   // block indices are >= 0
-        const uint64_t ob = (uint64_t)(uint32_t)pb * blk_stride;
+        // sub-block index of each unit: block << kSubShift | unit within it
+        // (block indices are >= 0)
+        constexpr uint32_t kSubMask = (1u << kSubShift) - 1;
+        const uint64_t oa = (uint64_t)(((uint32_t)pa << kSubShift) | ((uint32_t)ja & kSubMask)) * sub_stride;
+        const uint64_t ob = (uint64_t)(((uint32_t)pb << kSubShift) | ((uint32_t)jb & kSubMask)) * sub_stride;
 #pragma unroll
         for (int k = 0; k < kPerWave; ++k) {
             const int q = w + kWaves * k, reg = q / kCopies;
-            const int j = (reg & 1) ? jb : ja;
-            const int sub = j & ((1 << kSubShift) - 1);
-            const char* base = (reg < 2 ? kbase + sub * T::kUnitK : vbase + sub * T::kUnitV) +
-                               ((reg & 1) ? ob : oa);
+            const char* base = (reg < 2 ? kbase : vbase) + ((reg & 1) ? ob : oa);
             const int dst = (reg == 0 ? 0 : reg == 1 ? kOffKB : reg == 2 ? kOffVA : kOffVB) +
                             (q % kCopies) * 1024;
             copy16_to_lds(base, voff[k], lds_addr(st + dst));

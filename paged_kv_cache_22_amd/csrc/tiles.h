@@ -1,31 +1,31 @@
-// Per-KV-dtype access to one (block, kv-head) tile of the paged cache, in the
-// MFMA operand layouts the attention kernels use.  gfx950 / CDNA4.
+// Per-KV-dtype access to one 16-token tile of the paged cache, in the MFMA
+// operand layouts the attention kernels use.  gfx950 / CDNA4.
 //
-// A K tile is [D*eb/16 chunks][BS tokens][16 bytes]: 16-byte chunks of
-// consecutive dims with the token index inside each chunk.  A V tile is
-// [D][BS tokens] (dim-major).  BS, the cache block size, is 16, 32 or 64;
-// the kernels work in 16-token units, unit u of a block starting 16u tokens
-// into each K chunk run and each V row.  Both products of attention then read their
-// MFMA operands as whole contiguous runs: for the score product
-// S^T = K . Q^T (contraction over dims) lane (r, c) takes chunk 4i + c of
-// token r, so one load instruction of the wave reads 1 KiB in one piece; for
-// the output product O^T = V^T . P^T (contraction over tokens) lane (r, c)
-// takes tokens 4c..4c+3 of dim 16n + r, so one instruction reads 16 whole
-// dim rows.
+// The cache is made of 16-token sub-blocks: a cache block of BS tokens (16,
+// 32 or 64) is BS / 16 consecutive sub-blocks, each holding the tiles of all
+// kv-heads for its 16 tokens, so every (sub-block, kv-head) tile has the
+// same shape whatever the block size.  A K tile is [D*eb/16 chunks][16
+// tokens][16 bytes]: 16-byte chunks of consecutive dims with the token index
+// inside each chunk.  A V tile is [D][16 tokens] (dim-major).  Both products
+// of attention then read their MFMA operands as whole contiguous runs: for
+// the score product S^T = K . Q^T (contraction over dims) lane (r, c) takes
+// chunk 4i + c of token r, so one load instruction of the wave reads 1 KiB
+// in one piece; for the output product O^T = V^T . P^T (contraction over
+// tokens) lane (r, c) takes tokens 4c..4c+3 of dim 16n + r, so one
+// instruction reads 16 whole dim rows.
 #pragma once
 
 #include "device.h"
 
 namespace pa {
 
-constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hold 1, 2 or 4 units
+constexpr int kBS = 16;  // tokens per unit (MFMA tile height) = tokens of a sub-block
 
 // ---------------------------------------------------------------------------
 // Per-KV-dtype tile access.  For every kind:
-//   Regs  the lane's share of one block's K and V tile
+//   Regs  the lane's share of one tile's K and V
 //   QOp   the lane's share of Q^T, the B operand of the score MFMAs
-//   load  issues the global loads of one 16-token unit (kt, vt: the unit's
-//         start; BS: the block's token count, the K chunk and V row stride)
+//   load  issues the global loads of one 16-token tile (kt, vt: its start)
 //   qk    S^T fragment: lane (r, c) gets scores of head r, tokens 4c..4c+3
 //   pv    acc[n] += V^T[16n..16n+15, tokens] . P^T for this block
 // and for prefill, which stages two 16-token units (A, B) of K and V in LDS
@@ -37,9 +37,9 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 //   KRegs / load_k_xy    the K operands of X and Y from the staged units: a
 //                        unit's LDS copy holds the rows of X, then those of
 //                        Y, each as [chunk][8 rows][16 bytes]; k_lds_hbm maps
-//                        a byte of that copy to its place in the block tile
+//                        a byte of that copy to its place in the tile
 //   v_slot_hbm           where the 16-byte piece of LDS slot s of a staged V
-//                        unit comes from in the block tile
+//                        unit comes from in the tile
 // Both layouts are free of LDS bank conflicts for 16-byte reads, which gfx950
 // serves 16 lanes at a time -- lanes 0-7 with 24-31 and 8-15 with 16-23, the
 // same in the upper half-wave -- two lanes of one such pass conflicting when
@@ -50,21 +50,10 @@ constexpr int kBS = 16;  // tokens per unit (MFMA tile height); cache blocks hol
 //   mask_v_xy            zero the V of tokens at or past `valid`
 //   pv_xy  acc[n] += V^T . P^T over the 32 tokens; lsum2 the weights' sums
 // ---------------------------------------------------------------------------
-template <int KIND, int D, int BS = kBS> struct Tile;
+template <int KIND, int D> struct Tile;
 
-// Decode loads a unit's K as whole 128-byte lines whatever the block size,
-// but a unit's V is a 16-token slice of each BS-token row: with 32- or
-// 64-token blocks the units of a block (taken by different waves at about
-// the same time) share every V line.  Those V loads keep the line in L2 for
-// its siblings instead of streaming it past (with streaming V loads the
-// 64-token batch fetched 1.46x its live bytes from HBM).
-template <int BS> constexpr bool kVStreamFor = BS == kBS;
-
-template <int D, int BS> struct Tile<KV_BF16, D, BS> {
-    static constexpr bool kVStream = kVStreamFor<BS>;
-    static constexpr int kTileBytes = BS * D * 2;     // one (block, kv-head) tile
-    static constexpr int kUnitBytes = kBS * D * 2;    // one 16-token unit
-    static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 2;  // unit offsets in K runs / V rows
+template <int D> struct Tile<KV_BF16, D> {
+    static constexpr int kTileBytes = kBS * D * 2;    // one (sub-block, kv-head) tile
     static constexpr int KL = D / 32;  // 16-byte K loads per lane = score MFMAs
     static constexpr int NT = D / 16;  // 16-dim tiles of the output
     struct Regs { u32x4 k[KL]; u32x2 v[NT]; };
@@ -78,17 +67,14 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const char* p = vt + (16 * n + r) * (BS * 2) + c * 8;
-            R.v[n] = kVStream ? ldkv8(p) : ld8(p);
-        }
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv8(vt + (16 * n + r) * (kBS * 2) + c * 8);
     }
     __device__ static void settle(Regs&) {}   // loads land in MFMA layout
     struct KRegs { u32x4 k[KL]; };
     // V slot s = 2 * row + h holds tokens 8h..8h+7 of dim row
-    __device__ static int v_slot_hbm(int slot) { return (slot >> 1) * (BS * 2) + (slot & 1) * 16; }
+    __device__ static int v_slot_hbm(int slot) { return (slot >> 1) * (kBS * 2) + (slot & 1) * 16; }
     struct VOp { u32x4 v[NT]; };
     __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
 #pragma unroll
@@ -143,11 +129,8 @@ template <int D, int BS> struct Tile<KV_BF16, D, BS> {
     }
 };
 
-template <int D, int BS> struct Tile<KV_FP8, D, BS> {
-    static constexpr bool kVStream = kVStreamFor<BS>;
-    static constexpr int kTileBytes = BS * D;
-    static constexpr int kUnitBytes = kBS * D;
-    static constexpr int kUnitK = kBS * 16, kUnitV = kBS;
+template <int D> struct Tile<KV_FP8, D> {
+    static constexpr int kTileBytes = kBS * D;
     static constexpr int KL = D / 64;  // 16-byte K loads per lane, 16 codes = two MFMAs each
     static constexpr int NT = D / 16;
     struct Regs { u32x4 k[KL]; unsigned v[NT]; };
@@ -167,11 +150,10 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
     // word c of dim 16n + r to lane (r, c) as v[n], the layout pv() takes
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
         for (int m = 0; m < NT / 4; ++m) {
-            const char* p = vt + (16 * (4 * m + c) + r) * BS;
-            const u32x4 w = kVStream ? ldkv16(p) : ld16(p);
+            const u32x4 w = ldkv16(vt + (16 * (4 * m + c) + r) * kBS);
             R.v[4 * m] = w.x;
             R.v[4 * m + 1] = w.y;
             R.v[4 * m + 2] = w.z;
@@ -184,7 +166,7 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
     }
     struct KRegs { u32x4 k[KL]; };
     // V slot s is the unit's 16-token row of dim s (one 16-byte piece)
-    __device__ static int v_slot_hbm(int slot) { return slot * BS; }
+    __device__ static int v_slot_hbm(int slot) { return slot * kBS; }
     struct VOp { u32x2 v[NT]; };   // codes of tokens 8(c & 1) .. +7
     __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
 #pragma unroll
@@ -246,11 +228,8 @@ template <int D, int BS> struct Tile<KV_FP8, D, BS> {
     }
 };
 
-template <int D, int BS> struct Tile<KV_F32, D, BS> {
-    static constexpr bool kVStream = kVStreamFor<BS>;
-    static constexpr int kTileBytes = BS * D * 4;
-    static constexpr int kUnitBytes = kBS * D * 4;
-    static constexpr int kUnitK = kBS * 16, kUnitV = kBS * 4;
+template <int D> struct Tile<KV_F32, D> {
+    static constexpr int kTileBytes = kBS * D * 4;
     static constexpr int KL = D / 16;  // 16-byte K loads per lane, four MFMAs each
     static constexpr int NT = D / 16;
     struct Regs { u32x4 k[KL]; u32x4 v[NT]; };
@@ -264,17 +243,14 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
     }
     __device__ static void load(Regs& R, const char* kt, const char* vt, int r, int c) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * BS + r) * 16);
+        for (int i = 0; i < KL; ++i) R.k[i] = ldkv16(kt + ((4 * i + c) * kBS + r) * 16);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const char* p = vt + (16 * n + r) * (BS * 4) + c * 16;
-            R.v[n] = kVStream ? ldkv16(p) : ld16(p);
-        }
+        for (int n = 0; n < NT; ++n) R.v[n] = ldkv16(vt + (16 * n + r) * (kBS * 4) + c * 16);
     }
     __device__ static void settle(Regs&) {}
     struct KRegs { u32x4 k[KL]; };
     // V slot s = 4 * row + j holds tokens 4j..4j+3 of dim row
-    __device__ static int v_slot_hbm(int slot) { return (slot >> 2) * (BS * 4) + (slot & 3) * 16; }
+    __device__ static int v_slot_hbm(int slot) { return (slot >> 2) * (kBS * 4) + (slot & 3) * 16; }
     struct VOp { u32x4 a[NT], b[NT]; };   // tokens 8(c & 1) + 0..3 and + 4..7
     __device__ static void load_v_xy(VOp& V, const char* vu, int r, int c) {
 #pragma unroll
@@ -345,14 +321,14 @@ template <int D, int BS> struct Tile<KV_F32, D, BS> {
 // K of one staged unit in LDS: the rows of X (tokens 0-3 and 8-11), then
 // those of Y (tokens 4-7 and 12-15), each half [chunk][8 rows][16 bytes];
 // row rr of a half is token 8 * ((rr >> 2) & 1) + (rr & 3), + 4 in Y.
-// k_lds_hbm: the block-tile byte (unit 0) of LDS byte b of that copy.
-template <class T, int BS>
+// k_lds_hbm: the tile byte of LDS byte b of that copy.
+template <class T>
 __device__ __forceinline__ int k_lds_hbm(int b) {
-    constexpr int HK = T::kUnitBytes / 2;
+    constexpr int HK = T::kTileBytes / 2;
     const int xy = b / HK, bb = b % HK;
     const int chunk = bb >> 7, rr = (bb >> 4) & 7;
     const int tok = 8 * ((rr >> 2) & 1) + (rr & 3) + 4 * xy;
-    return chunk * (BS * 16) + tok * 16;
+    return chunk * (kBS * 16) + tok * 16;
 }
 
 // K operands of the score products X and Y from two staged units (kA, kB:
@@ -362,7 +338,7 @@ __device__ __forceinline__ int k_lds_hbm(int b) {
 template <class T>
 __device__ __forceinline__ void load_k_xy(typename T::KRegs& X, typename T::KRegs& Y,
                                           const char* kA, const char* kB, int r, int c) {
-    constexpr int HK = T::kUnitBytes / 2;
+    constexpr int HK = T::kTileBytes / 2;
     const char* ku = (r >> 3) ? kB : kA;
 #pragma unroll
     for (int i = 0; i < T::KL; ++i) {

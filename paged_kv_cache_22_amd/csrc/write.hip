@@ -151,9 +151,10 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
     const int h = hc / nchunk;
     const int j = hc - h * nchunk;
     const int tbase = tg * (16 * TPL) + r;
-    const int bs = a.block_size;          // 16, 32 or 64
-    const int bs_shift = bs == 64 ? 6 : bs == 32 ? 5 : 4;
-    const int cap = a.num_blocks * bs;
+    // a block of 16, 32 or 64 tokens is 1, 2 or 4 consecutive 16-token
+    // sub-blocks, so slot s is offset s mod 16 of sub-block s / 16 whatever
+    // the block size
+    const int cap = a.num_blocks * a.block_size;
 
     // All loads first and unconditionally, so that they are all in flight
     // together: a token past the end reads the last token's row (always
@@ -220,13 +221,13 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
             kw = kraw[i][0];
             vw = vraw[i][0];
         }
-        const int blk = slot[i] >> bs_shift;
-        const int off = slot[i] & (bs - 1);
-        const size_t tile = (size_t)blk * a.num_kv_heads + h;    // (block, kv-head) tile
+        const int blk = slot[i] >> 4;         // sub-block
+        const int off = slot[i] & (kUnit - 1);
+        const size_t tile = (size_t)blk * a.num_kv_heads + h;    // (sub-block, kv-head) tile
         // K: chunk j of the tile, 16 bytes at token offset `off`
         if (live)
             *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) +
-                                      ((tile * nchunk + j) * bs + off) * 16) = kw;
+                                      ((tile * nchunk + j) * kUnit + off) * 16) = kw;
         if (whole) {
             // V through LDS: the wave's four chunks of the 16 tokens cover the
             // unit's 16 * element bytes of 4X dim rows (hc0's first dim ..
@@ -237,23 +238,22 @@ __global__ __launch_bounds__(64 * kWaves) void write_kv_kernel(const WriteArgs a
             const u32x4 o = transposed_v<KV>(reinterpret_cast<const uint8_t*>(stage[w]), lane);
             __builtin_amdgcn_wave_barrier();
             const int j0 = (hc0 - h * nchunk);
-            const int off0 = s0 & (bs - 1);   // the unit's first token in the block
             const size_t vrow = tile * d + (size_t)j0 * X + lane / kCacheBytes;
-            char* vdst = static_cast<char*>(a.v_cache) + (vrow * bs + off0) * kCacheBytes +
+            char* vdst = static_cast<char*>(a.v_cache) + vrow * kUnit * kCacheBytes +
                          16 * (lane % kCacheBytes);
             *reinterpret_cast<u32x4*>(vdst) = o;
         } else if (live) {
             // V: dims j*X .. j*X+X-1 of the tile, one element per dim row at `off`
             char* vdst = static_cast<char*>(a.v_cache) +
-                         ((tile * d + (size_t)j * X) * bs + off) * kCacheBytes;
+                         ((tile * d + (size_t)j * X) * kUnit + off) * kCacheBytes;
 #pragma unroll
             for (int e = 0; e < X; ++e) {
                 if constexpr (KV == KV_FP8)
-                    reinterpret_cast<uint8_t*>(vdst)[e * bs] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
+                    reinterpret_cast<uint8_t*>(vdst)[e * kUnit] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
                 else if constexpr (KV == KV_BF16)
-                    reinterpret_cast<uint16_t*>(vdst)[e * bs] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+                    reinterpret_cast<uint16_t*>(vdst)[e * kUnit] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
                 else
-                    reinterpret_cast<unsigned*>(vdst)[e * bs] = vw[e];
+                    reinterpret_cast<unsigned*>(vdst)[e * kUnit] = vw[e];
             }
         }
     }

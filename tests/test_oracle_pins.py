@@ -36,17 +36,22 @@ with open(GOLD) as _f:
 def scatter_to_pages(Ks, Vs, bs, rng, extra_blocks=3, fill=np.nan, x=None):
     """Ks[b]: [L_b, Hkv, d] float64.  Returns pools, table, lens with a random
     physical placement; unused slots hold ``fill``.  K chunks hold x dims
-    (4 when d allows, else d)."""
+    (4 when d allows, else d).  The layout, written out here on its own: a
+    block of bs tokens is bs / 16 sub-blocks of 16 slots; K element
+    (block, sub-block, kv-head, chunk, slot, lane) is dim chunk * x + lane of
+    the token at slot 16 * sub-block + slot, V element (block, sub-block,
+    kv-head, dim, slot) likewise; 16-token blocks drop the sub-block axis."""
     B = len(Ks)
     Hkv, d = Ks[0].shape[1], Ks[0].shape[2]
     if x is None:
         x = 4 if d % 4 == 0 else d
+    n = bs // 16
     lens = np.array([k.shape[0] for k in Ks], dtype=np.int32)
     nblk = [-(-int(L) // bs) for L in lens]
     nb = sum(nblk) + extra_blocks
     perm = rng.permutation(nb)
-    kp = np.full((nb, Hkv, d // x, bs, x), fill)
-    vp = np.full((nb, Hkv, d, bs), fill)
+    kp = np.full((nb, n, Hkv, d // x, 16, x), fill)
+    vp = np.full((nb, n, Hkv, d, 16), fill)
     table = np.full((B, max(max(nblk), 1)), -1, dtype=np.int32)
     pos = 0
     for b in range(B):
@@ -56,9 +61,16 @@ def scatter_to_pages(Ks, Vs, bs, rng, extra_blocks=3, fill=np.nan, x=None):
             for slot in range(bs):
                 t = jb * bs + slot
                 if t < lens[b]:
-                    kp[phys, :, :, slot, :] = Ks[b][t].reshape(Hkv, d // x, x)
-                    vp[phys, :, :, slot] = Vs[b][t]
+                    kp[phys, slot // 16, :, :, slot % 16, :] = Ks[b][t].reshape(Hkv, d // x, x)
+                    vp[phys, slot // 16, :, :, slot % 16] = Vs[b][t]
+    if n == 1:
+        kp, vp = kp[:, 0], vp[:, 0]
     return kp, vp, table, lens
+
+
+def kvh(kp):
+    """kv-heads of a K pool built above."""
+    return kp.shape[1] if kp.ndim == 5 else kp.shape[2]
 
 
 def sdpa(q, K, V, scale, mask=None):
@@ -147,7 +159,7 @@ def test_quantiser_maps_amax_to_448():
 def test_decode_matches_dense_sdpa(seed, bs):
     q, Ks, Vs, kp, vp, table, lens = rand_decode_case(seed, bs=bs)
     B, Hq, d = q.shape
-    Hkv = kp.shape[1]
+    Hkv = kvh(kp)
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(d)
     out, lse = oracle.decode(f32(q), f32(kp), f32(vp), table, lens, scale, "f32", "f32")
@@ -184,7 +196,7 @@ def test_prefill_matches_dense_sdpa_bottom_right(seed, bs):
     q_lens, ctx_lens = [5, 17, 40], [0, 33, 9]
     q, cu, Ks, Vs, kp, vp, table, lens = _prefill_case(seed, q_lens, ctx_lens, bs=bs)
     Hq, d = q.shape[1], q.shape[2]
-    G = Hq // kp.shape[1]
+    G = Hq // kvh(kp)
     scale = 1.0 / math.sqrt(d)
     out, _ = oracle.prefill_chunk(f32(q), cu, f32(kp), f32(vp), table, lens, scale, "f32", "f32")
     for c in range(len(q_lens)):
@@ -200,7 +212,7 @@ def test_prefill_without_context_is_plain_causal():
     """ctx = 0: bottom-right and top-left alignment coincide, so torch's own
     is_causal path is a second, mask-free pin."""
     q, cu, Ks, Vs, kp, vp, table, lens = _prefill_case(3, [23], [0])
-    G = q.shape[1] // kp.shape[1]
+    G = q.shape[1] // kvh(kp)
     scale = 0.3
     out, _ = oracle.prefill_chunk(f32(q), cu, f32(kp), f32(vp), table, lens, scale, "f32", "f32")
     K = expand_gqa(f32(Ks[0]).astype(np.float64).transpose(1, 0, 2), G)
@@ -461,7 +473,7 @@ def test_mutation_wrong_gqa_mapping(monkeypatch):
     def bad_decode(q, k_cache, v_cache, block_table, seq_lens, scale, q_dtype, kv_dtype,
                    k_scale=None, v_scale=None, items=None):
         B, Hq, d = q.shape
-        Hkv = k_cache.shape[1]
+        Hkv = A.kv_heads(k_cache)
         qf = A.widen(q, q_dtype)
         out = np.zeros((B, Hq, d)); lse = np.zeros((B, Hq))
         for b in range(B):

@@ -13,6 +13,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -85,6 +86,38 @@ def test_write_positions_by_layout_formula():
     for s in untouched:
         blk, off = divmod(s, bs)
         assert np.isnan(kc[blk, :, :, off, :]).all() and np.isnan(vc[blk, :, :, off]).all()
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_write_positions_by_layout_formula_sub_blocks(bs):
+    """Blocks of 32 or 64 tokens are 16-token sub-blocks: K element (t, h,
+    dim) of slot = blk * bs + off lands at k_cache[blk, off // 16, h,
+    dim // X, off % 16, dim % X], the V element at v_cache[blk, off // 16, h,
+    dim, off % 16]; every other position is left alone."""
+    rng = np.random.default_rng(3)
+    T, Hkv, d, NB, X = 9, 2, 32, 3, 4
+    n = bs // 16
+    key = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+    val = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+    slots = rng.permutation(NB * bs)[:T].astype(np.int32)
+    slots[2] = -1
+    kc = np.full((NB, n, Hkv, d // X, 16, X), np.nan, np.float32)
+    vc = np.full((NB, n, Hkv, d, 16), np.nan, np.float32)
+    oracle.write_kv(kc, vc, key, val, slots, "f32", "f32")
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), bs)
+        for h in range(Hkv):
+            for dim in range(d):
+                assert kc[blk, off // 16, h, dim // X, off % 16, dim % X] == key[t, h, dim]
+                assert vc[blk, off // 16, h, dim, off % 16] == val[t, h, dim]
+    written = {int(s) for s in slots if s >= 0}
+    for s in range(NB * bs):
+        if s not in written:
+            blk, off = divmod(s, bs)
+            assert np.isnan(kc[blk, off // 16, :, :, off % 16, :]).all()
+            assert np.isnan(vc[blk, off // 16, :, :, off % 16]).all()
 
 
 def test_write_fp8_codes_and_round_trip_attention():

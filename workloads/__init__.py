@@ -12,12 +12,18 @@ Storage conventions (raw bits, so that each consumer widens them itself):
   from an fp32 draw, done by torch's CPU cast)
 * ``"fp8"``  -> ``numpy.uint8``   (OCP e4m3fn codes; one fp32 scale per kv-head)
 
-Cache layout (one contiguous tile per (block, kv-head)):
+Cache layout: a block of ``block_size`` tokens (16, 32 or 64) is
+``n = block_size / 16`` consecutive 16-token sub-blocks, each holding one
+contiguous tile per kv-head:
 
-* ``k_cache[num_blocks, num_kv_heads, head_dim/X, block_size, X]`` with X the
-  dims in 16 bytes (4 fp32, 8 bf16, 16 fp8): 16-byte chunks of consecutive
-  dims, the token index inside each chunk
-* ``v_cache[num_blocks, num_kv_heads, head_dim, block_size]``  dim-major
+* ``k_cache[num_blocks, n, num_kv_heads, head_dim/X, 16, X]`` with X the dims
+  in 16 bytes (4 fp32, 8 bf16, 16 fp8): 16-byte chunks of consecutive dims,
+  the token index inside each chunk
+* ``v_cache[num_blocks, n, num_kv_heads, head_dim, 16]``  dim-major
+
+For 16-token blocks (n = 1) the arrays are stored without the ``n`` axis:
+``k_cache[num_blocks, num_kv_heads, head_dim/X, 16, X]``,
+``v_cache[num_blocks, num_kv_heads, head_dim, 16]`` (the same bytes).
 
 The pages name block tables and sequence lengths as the metadata of the paged
 cache and say the platform fixes the cache layout (vllm-metal architecture
@@ -52,7 +58,7 @@ __all__ = [
     "decode_workload", "prefill_workload", "to_bf16_bits", "to_fp8_codes",
     "WriteWorkload", "write_workload", "write_chunks", "write_decode_step",
     "SharedPrefixWorkload", "shared_prefix_workload",
-    "kv_bytes_per_token", "CONFIG_NAMES",
+    "kv_bytes_per_token", "CONFIG_NAMES", "cache_shapes", "block_size_of", "to_cache_layout",
 ]
 
 CONFIG_NAMES = {
@@ -87,6 +93,38 @@ def to_fp8_codes(x: np.ndarray, scale: np.ndarray, axis_scale: int) -> np.ndarra
     y = torch.from_numpy(np.ascontiguousarray(x / s, dtype=np.float32))
     y = y.clamp_(-FP8_MAX, FP8_MAX)
     return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                 kv_dtype: str):
+    """Shapes of k_cache and v_cache (see the module docstring)."""
+    x = chunk_dims(kv_dtype)
+    n = block_size // 16
+    if block_size not in (16, 32, 64):
+        raise ValueError("block_size must be 16, 32 or 64")
+    if n == 1:
+        return ((num_blocks, num_kv_heads, head_dim // x, 16, x),
+                (num_blocks, num_kv_heads, head_dim, 16))
+    return ((num_blocks, n, num_kv_heads, head_dim // x, 16, x),
+            (num_blocks, n, num_kv_heads, head_dim, 16))
+
+
+def block_size_of(v_cache) -> int:
+    """Tokens per block of a v_cache array in this layout."""
+    return 16 if v_cache.ndim == 4 else 16 * int(v_cache.shape[1])
+
+
+def to_cache_layout(k, v, block_size: int):
+    """Pools drawn as [NB, Hkv, d/X, block_size, X] / [NB, Hkv, d, block_size]
+    (the token index running over the whole block) -> the sub-block layout."""
+    if block_size == 16:
+        return k, v
+    nb, hkv, nck, bs, x = k.shape
+    d = v.shape[2]
+    n = bs // 16
+    k = np.ascontiguousarray(k.reshape(nb, hkv, nck, n, 16, x).transpose(0, 3, 1, 2, 4, 5))
+    v = np.ascontiguousarray(v.reshape(nb, hkv, d, n, 16).transpose(0, 3, 1, 2, 4))
+    return k, v
 
 
 def chunk_dims(kv_dtype: str) -> int:
@@ -133,9 +171,9 @@ class DecodeWorkload:
     @property
     def head_dim(self) -> int: return int(self.q.shape[-1])
     @property
-    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
+    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1 if self.k_cache.ndim == 5 else 2])
     @property
-    def block_size(self) -> int: return int(self.v_cache.shape[3])
+    def block_size(self) -> int: return block_size_of(self.v_cache)
     @property
     def num_blocks(self) -> int: return int(self.k_cache.shape[0])
     @property
@@ -179,9 +217,9 @@ class PrefillWorkload:
     @property
     def head_dim(self) -> int: return int(self.q.shape[2])
     @property
-    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1])
+    def num_kv_heads(self) -> int: return int(self.k_cache.shape[1 if self.k_cache.ndim == 5 else 2])
     @property
-    def block_size(self) -> int: return int(self.v_cache.shape[3])
+    def block_size(self) -> int: return block_size_of(self.v_cache)
     @property
     def num_blocks(self) -> int: return int(self.k_cache.shape[0])
     @property
@@ -278,6 +316,7 @@ def _make_pools(seed, nb, hkv, d, bs, kv_dtype):
     if kv_dtype == "fp8":
         k, ks = _quantise_pool_fp8(k, hkv)
         v, vs = _quantise_pool_fp8(v, hkv)
+    k, v = to_cache_layout(k, v, bs)
     return k, v, ks, vs
 
 
@@ -439,7 +478,7 @@ class WriteWorkload:
     @property
     def num_blocks(self) -> int: return int(self.k_cache.shape[0])
     @property
-    def block_size(self) -> int: return int(self.v_cache.shape[3])
+    def block_size(self) -> int: return block_size_of(self.v_cache)
 
     def bytes_moved(self) -> int:
         """Algorithmic HBM bytes of one write: every token's K and V rows and
@@ -492,10 +531,8 @@ def write_workload(*, seed: int, slot_mapping, num_kv_heads: int, head_dim: int,
         amax = lambda x: np.abs(x).max(axis=(0, 2)) if T else np.ones(num_kv_heads, np.float32)
         ks = (amax(kf).astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
         vs = (amax(vf).astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
-    x = chunk_dims(kv_dtype)
     st = _STORAGE[kv_dtype]
-    kshape = (num_blocks, num_kv_heads, head_dim // x, block_size, x)
-    vshape = (num_blocks, num_kv_heads, head_dim, block_size)
+    kshape, vshape = cache_shapes(num_blocks, num_kv_heads, head_dim, block_size, kv_dtype)
     nbytes = int(np.prod(kshape)) * np.dtype(st).itemsize
     if fill_cache:
         crng = np.random.default_rng([seed, 8])
