@@ -132,7 +132,8 @@ int pa_version(void);
  * ceil(max_seq_len / partition_size); for PA_PARTITION_BALANCED room for
  * num_seqs piece records (2 int32) and the partials of up to
  * 1024 + num_seqs pieces of num_q_heads rows each.  Each region is 256-byte
- * aligned.  Returns 0 for invalid arguments.
+ * aligned.  Returns 0 for invalid arguments and for sizes the decode calls
+ * refuse (num_seqs * num_q_heads above 2^31 - 1, more than 65535 partitions).
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                 int max_seq_len, int partition_size);
@@ -274,8 +275,9 @@ int pa_decode_stages(void* out, const void* q, int q_dtype, int q_len,
  * partition_size (> 0) tokens; (3) the log-sum-exp merge of both.
  * q, out [num_seqs, q_len, num_q_heads, head_dim] (q_len * G <= 16; q_len 1
  * is plain decode); workspace of at least
- * pa_decode_shared_prefix_workspace_size(...) bytes.  prefix_len 0 is
- * pa_decode_multi_query in one pass.
+ * pa_decode_shared_prefix_workspace_size(...) bytes (0 for invalid arguments
+ * and sizes the call refuses).  prefix_len 0 is pa_decode_multi_query in one
+ * pass.
  */
 size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int q_len, int num_q_heads,
                                               int num_kv_heads, int head_dim, int prefix_len,
