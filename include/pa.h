@@ -153,7 +153,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
  * pa_merge_partitions) writes out.  A sequence that fits in one partition
  * is written directly by the partition kernel (bit-identical to merging its
- * single partition).  A workspace serves one call at a time.
+ * single partition).  When max_seq_len spans at least 16 partitions and a
+ * partition is a multiple of 64 tokens (bf16 and fp8 KV), the partitions
+ * are streamed: each workgroup takes a run of consecutive partitions, the
+ * runs balanced over the batch and the device's resident workgroups, and
+ * its loads run on across partition boundaries; every partition's result
+ * is bit-identical to the one-workgroup-per-partition kernel's, so this
+ * changes time, not results.  A workspace serves one call at a time.
  *
  * partition_size == PA_PARTITION_BALANCED: the blocks of all sequences, laid
  * end to end per kv-head, are cut into equal ranges, one per workgroup, with

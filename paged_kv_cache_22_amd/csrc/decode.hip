@@ -55,12 +55,61 @@ struct RangeOut {
     size_t prow_stride;
 };
 
+// Partition streaming (PARTS below) stages finished partials in LDS and
+// writes them in bulk: a wave's stores hold back the completion count of
+// every load it issues after them until they are acknowledged, which under
+// full read traffic takes longer than the next blocks' loads, and the
+// waves wait for each other at every partition boundary.  A slot holds the
+// G normalised rows and lse of one (partition, kv-head), and the index of
+// its first partial row.
+constexpr int kStageFloats = 18 * 256;   // 18 KiB of slots per workgroup
+constexpr int kMaxStageSlots = 32;
+
+struct Stage {
+    float* data;        // slots of `size` floats: cols rows of D, then cols lse
+    long long* base;    // [kMaxStageSlots]: partial index of a slot's row 0
+    int cols, size;     // rows per slot, floats per slot (a multiple of 4)
+    int slots;          // slots filled before a bulk store
+    int n;              // slots filled (workgroup-uniform)
+};
+
+// Every wave of the workgroup writes a share of the n staged slots to the
+// partials (row rr of slot j at partial index base[j] + rr * max_parts);
+// the caller has passed a barrier since the slots were written.
+template <int D, int WAVES>
+__device__ __forceinline__ void store_staged(const DecodeArgs& a, Stage& st) {
+    const int tid = threadIdx.x;
+    const int per = st.cols * D / 4;   // float4s of one slot's rows
+#pragma unroll 1
+    for (int j = 0; j < st.n; ++j) {
+        const float* slot = st.data + j * st.size;
+        const long long base = st.base[j];
+#pragma unroll 1
+        for (int q = tid; q < per; q += 64 * WAVES) {
+            const int rr = q / (D / 4), d4 = q % (D / 4);
+            *reinterpret_cast<f32x4*>(a.part_out + (base + (long long)rr * a.max_parts) * D + 4 * d4) =
+                *reinterpret_cast<const f32x4*>(slot + rr * D + 4 * d4);
+        }
+        if (tid < st.cols) a.part_lse[base + (long long)tid * a.max_parts] = slot[st.cols * D + tid];
+    }
+    st.n = 0;
+}
+
 // Attention of sequence b (L cached tokens), kv-head h, over its logical
 // blocks [j0, j1) by the workgroup's WAVES waves (j0 < j1).  Wave w takes
 // blocks j0 + w, j0 + w + WAVES, ...; wave 0 combines and writes.
-template <int D, int KIND, int BS, bool MQ, int WAVES>
+//
+// PARTS: [j0, j1) is a run of consecutive fixed partitions of upw * WAVES
+// blocks each (j0 on a partition boundary; only the last may be short), and
+// every partition gets its own result, exactly the one a workgroup given
+// that partition alone computes (the same blocks per wave, the same
+// combine).  The waves stream on across partition boundaries -- the next
+// blocks' loads are in flight while a finished partition's states are
+// combined.
+template <int D, int KIND, int BS, bool MQ, int WAVES, bool PARTS = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, int L, int j0, int j1,
-                                             const RangeOut& dst, float* smem) {
+                                             const RangeOut& dst, float* smem, int upw = 0,
+                                             Stage* stage = nullptr) {
     using T = Tile<KIND, D>;
     constexpr int kSubShift = BS == 64 ? 2 : BS == 32 ? 1 : 0;   // log2(sub-blocks per block)
     using QT = typename QType<KIND>::T;
@@ -166,6 +215,91 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
         T::pv(R, p, acc);
     };
 
+    // PARTS: the partitions of the range, and the wave's blocks in all but the last
+    const int nparts = PARTS ? (j1 - j0 + upw * WAVES - 1) / (upw * WAVES) : 1;
+    const int n_full = PARTS ? (nparts - 1) * upw : 0;
+    // PARTS: combine and reset the states of partition kk of the range, into
+    // a stage slot (or, for a sequence of one partition written directly,
+    // into the output)
+    auto flush = [&](int kk) {
+        if constexpr (PARTS) {
+            static_assert(!MQ, "partition streaming: one query per sequence");
+            float* s_acc = smem;                         // [WAVES][NT][64 lanes][4]
+            float* s_m = smem + WAVES * NT * 4 * 64;     // [WAVES][16]
+            float* s_l = s_m + WAVES * 16;               // [WAVES][16]
+            const float lsum = group_sum4(l);
+            __syncthreads();   // the previous partition's combine has read the LDS
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                *reinterpret_cast<f32x4*>(s_acc + ((w * NT + n) * 64 + lane) * 4) = acc[n];
+            if (c == 0) {
+                s_m[w * 16 + r] = m;
+                s_l[w * 16 + r] = lsum;
+            }
+            __syncthreads();
+            // each wave finishes NT / WAVES of the output tiles, in the order
+            // of the single-partition combine: wave 0's state scaled first,
+            // then waves 1, 2, ... added
+            constexpr int TW = NT / WAVES;
+            static_assert(NT % WAVES == 0, "whole output tiles per wave");
+            float M = s_m[r];
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v) M = fmaxf(M, s_m[v * 16 + r]);
+            float f = fast_exp2((s_m[r] - M) * C);
+            float lt = s_l[r] * f;
+            f32x4 o[TW];
+#pragma unroll
+            for (int t = 0; t < TW; ++t)
+                o[t] = *reinterpret_cast<const f32x4*>(s_acc + ((w * TW + t) * 64 + lane) * 4) * f;
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v) {
+                f = fast_exp2((s_m[v * 16 + r] - M) * C);
+                lt += f * s_l[v * 16 + r];
+#pragma unroll
+                for (int t = 0; t < TW; ++t) {
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(
+                        s_acc + ((v * NT + w * TW + t) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[t][e] += f * sv[e];
+                }
+            }
+            if (col_ok) {
+                const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
+                const float inv = vscale / lt;
+                if (dst.direct) {
+#pragma unroll
+                    for (int t = 0; t < TW; ++t)
+                        store4(reinterpret_cast<QT*>(a.out) + row * D + 16 * (w * TW + t) + 4 * c,
+                               o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+                } else {
+                    float* slot = stage->data + stage->n * stage->size;
+#pragma unroll
+                    for (int t = 0; t < TW; ++t)
+                        store4(slot + r * D + 16 * (w * TW + t) + 4 * c, o[t][0] * inv,
+                               o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+                    if (w == 0 && c == 0) slot[stage->cols * D + r] = (M * C + fast_log2(lt)) * kLn2;
+                }
+            }
+            if (!dst.direct && threadIdx.x == 0)   // partial index of the slot's row 0
+                stage->base[stage->n] =
+                    (long long)(dst.prow_base + (size_t)kk + (row - r) * dst.prow_stride);
+            if (!dst.direct && ++stage->n == stage->slots) {
+                __syncthreads();   // the slots are written
+                store_staged<D, WAVES>(a, *stage);
+            }
+            m = -INFINITY;
+            l = 0.f;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[n] = zero4();
+        }
+    };
+    // PARTS: after the wave's block u, a partition other than the last ends
+    auto boundary = [&](int u) {
+        if constexpr (PARTS) {
+            if (u >= 0 && u < n_full && (u + 1) % upw == 0) flush(u / upw);
+        }
+    };
+
     // Two-stage software pipeline: block i+1 is in flight while block i is
     // computed.  The steady-state loop issues its loads unconditionally and
     // the tail is peeled, so the compiler's in-order load counting never
@@ -181,8 +315,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
                 tcur = tnxt;
                 tnxt = (tbase + 64 + lane < n_mine) ? trow[(ubase + (tbase + 64 + lane) * WAVES) >> kSubShift] : 0;
             }
+            boundary(i - 1);
             issue(b1, i + 1);
             consume(b0, i);
+            boundary(i);
             issue(b0, i + 2);
             consume(b1, i + 1);
         }
@@ -191,12 +327,21 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
             tcur = tnxt;
         }
         if (i + 1 < n_mine) {
+            boundary(i - 1);
             issue(b1, i + 1);
             consume(b0, i);
+            boundary(i);
             consume(b1, i + 1);
         } else {
+            boundary(i - 1);
             consume(b0, i);
         }
+        // a wave with no block in the last partition ends the one before here
+        boundary(n_mine - 1);
+    }
+    if constexpr (PARTS) {
+        flush(nparts - 1);
+        return;
     }
 
     l = group_sum4(l);
@@ -262,10 +407,12 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
 }
 
 
-// LDS floats of the waves' softmax-state combine
-template <int D, int KIND, int WAVES>
+// LDS floats of the waves' softmax-state combine (PARTS: every wave's
+// state, then the stage slots and their partial indices)
+template <int D, int KIND, int WAVES, bool PARTS = false>
 constexpr int combine_floats() {
-    constexpr int f = (WAVES - 1) * (Tile<KIND, D>::NT * 4 * 64 + 32);
+    constexpr int f = (PARTS ? WAVES : WAVES - 1) * (Tile<KIND, D>::NT * 4 * 64 + 32) +
+                      (PARTS ? kStageFloats + 2 * kMaxStageSlots : 0);
     return f > 1 ? f : 1;
 }
 
@@ -343,15 +490,30 @@ __device__ __forceinline__ int owner(long long x, long long W, int S) {
     return (int)(((x + 1) * S - 1) / W);
 }
 
-template <int D, int KIND, int BS, bool MQ, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const DecodeArgs a) {
-    __shared__ float smem[combine_floats<D, KIND, WAVES>()];
+//
+// PARTS: the same balance over the batch's fixed partitions instead of its
+// units: split s of S owns partitions [s*I/S, (s+1)*I/S) of the I =
+// sum_b ceil(units_b / PB) partitions laid end to end, and streams each
+// sequence's run of them with one attend_range.  Every partition's result is
+// the fixed-partition kernel's, bit for bit, at partial slot p + part_offset;
+// the workgroup only saves that kernel's per-partition pipeline refill.
+template <int D, int KIND, int BS, bool MQ, int WAVES, bool PARTS = false>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PARTS ? 3 : 1))) void decode_balanced_kernel(const DecodeArgs a) {
+    __shared__ __align__(16) float smem[combine_floats<D, KIND, WAVES, PARTS>()];
     const int lane = threadIdx.x & 63;
     const int s = blockIdx.x;
     const int h = blockIdx.y;
     const int B = a.num_seqs;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int cols = (MQ ? a.q_len : 1) * G;   // output rows of one (piece, kv-head)
+    const int PB = a.partition_blocks;
+    // what the split balances: a sequence's units, or (PARTS) its partitions,
+    // at most the grid_parts the caller's max_seq_len allows (the partial
+    // slots there are)
+    auto items = [&](int len) {
+        const int u = (len + kBS - 1) / kBS;
+        return PARTS ? min((u + PB - 1) / PB, a.grid_parts) : u;
+    };
 
     // W = sum of ceil(L / 16) over the batch.  Lane l owns the contiguous run
     // of sequences [l*C, min(B, (l+1)*C)), C = ceil(B / 64), and sums its run
@@ -369,7 +531,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
         }
         if (k0 == 0) len0 = v[0];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) mine += (v[k] + kBS - 1) / kBS;
+        for (int k = 0; k < 8; ++k) mine += items(v[k]);
     }
     const int incl = wave_incl_scan_i(mine);
     const int W = __builtin_amdgcn_readlane(incl, 63);
@@ -392,7 +554,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
         for (int k0 = 0; k0 < C; k0 += 64) {
             const int i = k0 + lane;
             const int Li = rb + i < B ? a.seq_lens[rb + i] : 0;
-            const int ni = (Li + kBS - 1) / kBS;
+            const int ni = items(Li);
             const int inc2 = wave_incl_scan_i(ni);
             const unsigned long long hit = __ballot(i < C && rb + i < B && cum + inc2 > start);
             if (hit) {
@@ -409,15 +571,39 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
 
     const size_t slots = (size_t)gridDim.x + B;  // the merge's piece_slots
     int2* info = reinterpret_cast<int2*>(a.piece_info);
+    Stage stage;   // PARTS: staged partials
+    if constexpr (PARTS) {
+        constexpr int kComb = WAVES * (Tile<KIND, D>::NT * 4 * 64 + 32);
+        stage.data = smem + kComb;
+        stage.base = reinterpret_cast<long long*>(smem + kComb + kStageFloats);
+        stage.cols = G;
+        stage.size = G * D + ((G + 3) & ~3);
+        stage.slots = min(kMaxStageSlots, kStageFloats / stage.size);
+        stage.n = 0;
+    }
     for (int pos = start; pos < end && b < B; ++b) {
         if (b - lb >= 64) {  // uniform: the next 64 lengths
             lb = b;
             lw = b + lane < B ? a.seq_lens[b + lane] : 0;
         }
         const int L = __builtin_amdgcn_readlane(lw, b - lb);
-        const int n = (L + kBS - 1) / kBS;
+        const int n = items(L);
         if (n == 0) continue;  // an empty sequence owns no unit (the merge writes its zeros)
         const int seg_end = min(end, cum + n);
+        if constexpr (PARTS) {
+            // partitions [pos - cum, seg_end - cum) of sequence b
+            const int p0 = pos - cum, p1 = seg_end - cum;
+            RangeOut dst;
+            dst.direct = n == 1 && a.single_direct;
+            dst.prow_base = (size_t)(p0 + a.part_offset);
+            dst.prow_stride = (size_t)a.max_parts;
+            attend_range<D, KIND, BS, false, WAVES, true>(
+                a, b, h, L, p0 * PB, min(p1 * PB, (L + kBS - 1) / kBS), dst, smem, PB / WAVES,
+                &stage);
+            pos = seg_end;
+            cum += n;
+            continue;
+        }
         const int s_first = owner(cum, W, S), s_last = owner(cum + n - 1, W, S);
         if (h == 0 && s == s_first && threadIdx.x == 0)
             info[b] = make_int2(s_first + b, s_last - s_first + 1);
@@ -429,6 +615,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_balanced_kernel(const Decod
         __syncthreads();  // the next piece reuses the combine LDS
         pos = seg_end;
         cum += n;
+    }
+    if constexpr (PARTS) {
+        if (stage.n > 0) {   // uniform
+            __syncthreads();   // the last slots are written
+            store_staged<D, WAVES>(a, stage);
+        }
     }
 }
 
@@ -445,6 +637,20 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int KIND, int BS, bool MQ, bool PARTS = false>
+int splits_t(int num_kv_heads);
+
+// Fixed partitions are streamed (several consecutive partitions per
+// workgroup, balanced over the batch) when sequences may hold at least this
+// many of them and a partition is a whole number of blocks per wave; not for
+// fp32 KV, whose streaming kernel would hold one wave per SIMD.  Below it
+// (batches of sequences a few partitions long) the dispatcher's balancing of
+// one workgroup per partition measured faster.
+#ifndef PA_STREAM_MIN_PARTS
+#define PA_STREAM_MIN_PARTS 16
+#endif
+constexpr int kStreamMinParts = PA_STREAM_MIN_PARTS;
+
 template <int D, int KIND, int BS, bool MQ>
 hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
     if (a.balanced) {
@@ -453,6 +659,17 @@ hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
                            0, s, a);
         return hipGetLastError();
     }
+    if constexpr (!MQ && KIND != KV_F32) {
+        if (a.partition_blocks > 0 && a.partition_blocks % kWaves == 0 &&
+            a.grid_parts >= kStreamMinParts) {
+            const int splits = splits_t<D, KIND, BS, false, true>(a.num_kv_heads);
+            if (splits < 1) return hipErrorInvalidValue;
+            dim3 grid((unsigned)splits, (unsigned)a.num_kv_heads);
+            hipLaunchKernelGGL((decode_balanced_kernel<D, KIND, BS, false, kWaves, true>), grid,
+                               dim3(64 * kWaves), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     return a.partition_blocks > 0 ? launch_t<D, KIND, BS, true, MQ>(a, s)
                                   : launch_t<D, KIND, BS, false, MQ>(a, s);
 }
@@ -460,7 +677,7 @@ hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
 // Balanced splits per kv-head: the workgroups of the balanced kernel that
 // the device holds at once (occupancy x compute units), shared by the
 // kv-heads, at most kMaxBalancedSplits.  Cached per device and variant.
-template <int D, int KIND, int BS, bool MQ>
+template <int D, int KIND, int BS, bool MQ, bool PARTS>
 int splits_t(int num_kv_heads) {
     constexpr int kDevices = 64;
     static int resident[kDevices];  // 0 = not yet known; a racing first call stores the same value
@@ -472,7 +689,7 @@ int splits_t(int num_kv_heads) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return -1;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, decode_balanced_kernel<D, KIND, BS, MQ, kWaves>, 64 * kWaves, 0) != hipSuccess)
+                &per_cu, decode_balanced_kernel<D, KIND, BS, MQ, kWaves, PARTS>, 64 * kWaves, 0) != hipSuccess)
             return -1;
 #ifdef PA_BALANCED_PER_CU
         per_cu = PA_BALANCED_PER_CU;  // build-time override of the occupancy
