@@ -55,27 +55,28 @@ struct RangeOut {
     size_t prow_stride;
 };
 
-// Partition streaming (PARTS below) stages finished partials in LDS and
-// writes them in bulk: a wave's stores hold back the completion count of
-// every load it issues after them until they are acknowledged, which under
-// full read traffic takes longer than the next blocks' loads, and the
-// waves wait for each other at every partition boundary.  A slot holds the
-// G normalised rows and lse of one (partition, kv-head), and the index of
-// its first partial row.
+// The balanced kernel stages finished partials (of its pieces, or with
+// PARTS below of its partitions) in LDS and writes them in bulk, at the end
+// or when the slots are full: partial stores in the middle of the stream
+// measured costly (on gfx950 a wave's stores share the load counter, and
+// under full read traffic they hold back the loads issued after them).  A
+// slot holds the normalised rows and lse of one (piece or partition,
+// kv-head) and the index of its first partial row.
 constexpr int kStageFloats = 18 * 256;   // 18 KiB of slots per workgroup
 constexpr int kMaxStageSlots = 32;
 
 struct Stage {
     float* data;        // slots of `size` floats: cols rows of D, then cols lse
     long long* base;    // [kMaxStageSlots]: partial index of a slot's row 0
+    long long stride;   // partial indices between a slot's rows
     int cols, size;     // rows per slot, floats per slot (a multiple of 4)
     int slots;          // slots filled before a bulk store
     int n;              // slots filled (workgroup-uniform)
 };
 
 // Every wave of the workgroup writes a share of the n staged slots to the
-// partials (row rr of slot j at partial index base[j] + rr * max_parts);
-// the caller has passed a barrier since the slots were written.
+// partials (row rr of slot j at partial index base[j] + rr * stride); the
+// caller has passed a barrier since the slots were written.
 template <int D, int WAVES>
 __device__ __forceinline__ void store_staged(const DecodeArgs& a, Stage& st) {
     const int tid = threadIdx.x;
@@ -87,10 +88,10 @@ __device__ __forceinline__ void store_staged(const DecodeArgs& a, Stage& st) {
 #pragma unroll 1
         for (int q = tid; q < per; q += 64 * WAVES) {
             const int rr = q / (D / 4), d4 = q % (D / 4);
-            *reinterpret_cast<f32x4*>(a.part_out + (base + (long long)rr * a.max_parts) * D + 4 * d4) =
+            *reinterpret_cast<f32x4*>(a.part_out + (base + rr * st.stride) * D + 4 * d4) =
                 *reinterpret_cast<const f32x4*>(slot + rr * D + 4 * d4);
         }
-        if (tid < st.cols) a.part_lse[base + (long long)tid * a.max_parts] = slot[st.cols * D + tid];
+        if (tid < st.cols) a.part_lse[base + tid * st.stride] = slot[st.cols * D + tid];
     }
     st.n = 0;
 }
@@ -106,6 +107,8 @@ __device__ __forceinline__ void store_staged(const DecodeArgs& a, Stage& st) {
 // combine).  The waves stream on across partition boundaries -- the next
 // blocks' loads are in flight while a finished partition's states are
 // combined.
+//
+// stage (balanced kernel): partials go to its slots instead of part_out.
 template <int D, int KIND, int BS, bool MQ, int WAVES, bool PARTS = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, int L, int j0, int j1,
                                              const RangeOut& dst, float* smem, int upw = 0,
@@ -385,6 +388,24 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
         }
     }
 
+    if (stage != nullptr && !dst.direct) {   // uniform: the balanced kernel's partials go to a stage slot
+        if (w == 0 && col_ok) {
+            const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
+            const float inv = (MQ && !(l > 0.f)) ? 0.f : vscale / l;
+            float* slot = stage->data + stage->n * stage->size;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                store4(slot + r * D + 16 * n + 4 * c, acc[n][0] * inv, acc[n][1] * inv,
+                       acc[n][2] * inv, acc[n][3] * inv);
+            if (c == 0) slot[stage->cols * D + r] = (m * C + fast_log2(l)) * kLn2;
+        }
+        if (threadIdx.x == 0) stage->base[stage->n] = (long long)dst.prow_base;
+        if (++stage->n == stage->slots) {
+            __syncthreads();   // the slots are written
+            store_staged<D, WAVES>(a, *stage);
+        }
+        return;
+    }
     if (w > 0 || !col_ok) return;
     const float vscale = KIND == KV_FP8 ? a.v_scale[h] : 1.0f;
     // l = 0 only for a column that saw no key (MQ): zeros, lse -inf
@@ -409,10 +430,10 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int b, int h, 
 
 // LDS floats of the waves' softmax-state combine (PARTS: every wave's
 // state, then the stage slots and their partial indices)
-template <int D, int KIND, int WAVES, bool PARTS = false>
+template <int D, int KIND, int WAVES, bool PARTS = false, bool STAGED = false>
 constexpr int combine_floats() {
     constexpr int f = (PARTS ? WAVES : WAVES - 1) * (Tile<KIND, D>::NT * 4 * 64 + 32) +
-                      (PARTS ? kStageFloats + 2 * kMaxStageSlots : 0);
+                      (STAGED ? kStageFloats + 2 * kMaxStageSlots : 0);
     return f > 1 ? f : 1;
 }
 
@@ -471,7 +492,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
 // directly; otherwise its pieces go to partial slot s + b (strictly
 // increasing along the pieces, so unique, and contiguous for one sequence)
 // and the first piece's workgroup of kv-head 0 records (first slot, count)
-// for the merge.
+// for the merge.  The partials are staged in LDS and stored at the end.
 // ---------------------------------------------------------------------------
 // inclusive prefix sum over the wave's 64 lanes: DPP row shifts within each
 // 16-lane row, then row broadcasts carry the row totals upward (no LDS)
@@ -498,8 +519,11 @@ __device__ __forceinline__ int owner(long long x, long long W, int S) {
 // the fixed-partition kernel's, bit for bit, at partial slot p + part_offset;
 // the workgroup only saves that kernel's per-partition pipeline refill.
 template <int D, int KIND, int BS, bool MQ, int WAVES, bool PARTS = false>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PARTS ? 3 : 1))) void decode_balanced_kernel(const DecodeArgs a) {
-    __shared__ __align__(16) float smem[combine_floats<D, KIND, WAVES, PARTS>()];
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KIND != KV_F32 ? 3 : 1))) void decode_balanced_kernel(const DecodeArgs a) {
+    // pieces' partials are staged in LDS (not with several queries, whose
+    // kernel would outgrow three waves per SIMD)
+    constexpr bool kStaged = PARTS || !MQ;
+    __shared__ __align__(16) float smem[combine_floats<D, KIND, WAVES, PARTS, kStaged>()];
     const int lane = threadIdx.x & 63;
     const int s = blockIdx.x;
     const int h = blockIdx.y;
@@ -571,13 +595,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PART
 
     const size_t slots = (size_t)gridDim.x + B;  // the merge's piece_slots
     int2* info = reinterpret_cast<int2*>(a.piece_info);
-    Stage stage;   // PARTS: staged partials
-    if constexpr (PARTS) {
-        constexpr int kComb = WAVES * (Tile<KIND, D>::NT * 4 * 64 + 32);
+    Stage stage;   // staged partials
+    if constexpr (kStaged) {
+        constexpr int kComb = (PARTS ? WAVES : WAVES - 1) * (Tile<KIND, D>::NT * 4 * 64 + 32);
         stage.data = smem + kComb;
         stage.base = reinterpret_cast<long long*>(smem + kComb + kStageFloats);
-        stage.cols = G;
-        stage.size = G * D + ((G + 3) & ~3);
+        stage.stride = PARTS ? a.max_parts : 1;
+        stage.cols = cols;
+        stage.size = cols * D + ((cols + 3) & ~3);
         stage.slots = min(kMaxStageSlots, kStageFloats / stage.size);
         stage.n = 0;
     }
@@ -611,12 +636,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(PART
         dst.direct = s_first == s_last;
         dst.prow_base = (((size_t)h * slots) + (size_t)(s + b)) * cols;
         dst.prow_stride = 0;
-        attend_range<D, KIND, BS, MQ, WAVES>(a, b, h, L, pos - cum, seg_end - cum, dst, smem);
+        attend_range<D, KIND, BS, MQ, WAVES>(a, b, h, L, pos - cum, seg_end - cum, dst, smem, 0,
+                                             kStaged ? &stage : nullptr);
         __syncthreads();  // the next piece reuses the combine LDS
         pos = seg_end;
         cum += n;
     }
-    if constexpr (PARTS) {
+    if constexpr (kStaged) {
         if (stage.n > 0) {   // uniform
             __syncthreads();   // the last slots are written
             store_staged<D, WAVES>(a, stage);
