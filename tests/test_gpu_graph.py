@@ -6,7 +6,8 @@ host synchronisation (vllm-metal architecture article, section 三).  The
 library's calls enqueue kernels only -- no allocation, no memset, no host
 read of device data -- so they can be captured.  Here one step is captured
 once: the cache write of each sequence's newest token, decode in the
-balanced mode and at 512-token partitions, and a causal prefill chunk.  Its
+balanced mode, at 512-token partitions and at 128-token partitions (up to
+24 per sequence: the streamed kernel), and a causal prefill chunk.  Its
 inputs (q, the new K/V rows and their slots, the sequence lengths) are then
 rewritten in place and the graph replayed several times, with eager work
 and synchronisations between the replays; every replay must equal, bit for
@@ -22,6 +23,7 @@ from gpu_util import compare, dev, f64, oracle_decode
 
 pytestmark = pytest.mark.gpu
 BAL = -1
+MODES = (BAL, 512, 128)
 
 
 def test_step_captured_in_a_graph_replays_like_eager_calls():
@@ -45,13 +47,13 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
     pk, pv, pbt, psl = dev(pw.k_cache, "bf16"), dev(pw.v_cache, "bf16"), dev(pw.block_table), \
         dev(pw.seq_lens)
     ws = {P: torch.empty(max(pa.decode_workspace_size(B, Hq, D, max_len, P), 256),
-                         dtype=torch.uint8, device="cuda") for P in (BAL, 512)}
-    outs = {P: torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda") for P in (BAL, 512)}
+                         dtype=torch.uint8, device="cuda") for P in MODES}
+    outs = {P: torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda") for P in MODES}
     pout = torch.empty_like(pq)
 
     def step():
         pa.write_kv(new_k, new_v, k, v, slots)
-        for P in (BAL, 512):
+        for P in MODES:
             pa.decode(q, k, v, bt, lens, max_seq_len=max_len, scale=wl.scale, partition_size=P,
                       out=outs[P], workspace=ws[P])
         pa.prefill_chunk(pq, pcu, pk, pv, pbt, psl, max_q_len=int(pw.max_q_len), scale=pw.scale,
@@ -73,8 +75,8 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
         torch.cuda.synchronize()
         return L
 
-    # eager warm-up: the balanced mode's one-time occupancy query runs here,
-    # outside the capture
+    # eager warm-up: the balanced and streamed kernels' one-time occupancy
+    # queries run here, outside the capture
     new_inputs()
     step()
     torch.cuda.synchronize()

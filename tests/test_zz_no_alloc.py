@@ -25,7 +25,7 @@ def _noalloc(d, P):
     return out
 
 
-@pytest.mark.parametrize("P", [BAL, 512, 0])
+@pytest.mark.parametrize("P", [BAL, 512, 128, 0])   # 128: up to 32 partitions, streamed
 def test_noalloc_equals_pa_decode_on_two_calls(P):
     big = W.config2()
     small = W.decode_workload(seed=301, num_seqs=7, num_q_heads=32, num_kv_heads=8, head_dim=128,
