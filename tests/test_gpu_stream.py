@@ -30,6 +30,8 @@ CASES = [
     ("fp8", 128, 16, 1, 32, 64, 600),
     ("bf16", 64, 40, 10, 16, 64, 100),
     ("bf16", 128, 16, 1, 16, 64, 600),
+    ("bf16", 128, 8, 1, 32, 128, 300),
+    ("fp8", 64, 8, 8, 64, 256, 100),
 ]
 
 
