@@ -148,7 +148,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * log-sum-exp is this library's (the pages give no rule for it).
  *
  * partition_size == 0: one pass per (sequence, kv-head), out written
- * directly.  partition_size > 0 (a multiple of 16 tokens): split-KV; each
+ * directly.  With at least 1024 (sequence, kv-head) pairs and at most 1024
+ * sequences the workgroups take the sequences longest first (each
+ * workgroup finds its sequence from seq_lens on the device), so the grid
+ * does not end on a tail of long sequences; results are unchanged.  partition_size > 0 (a multiple of 16 tokens): split-KV; each
  * partition p covers tokens [p*P, min((p+1)*P, L)) and writes its normalised
  * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
  * pa_merge_partitions) writes out.  A sequence that fits in one partition

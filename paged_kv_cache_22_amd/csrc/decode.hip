@@ -454,6 +454,104 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int b, int h) {
     for (int n = 0; n < T::NT; ++n) store4(o + 16 * n + 4 * c, 0.f, 0.f, 0.f, 0.f);
 }
 
+// inclusive prefix sum over the wave's 64 lanes: DPP row shifts within each
+// 16-lane row, then row broadcasts carry the row totals upward (no LDS)
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+// Longest sequences first (one-pass mode).  Workgroups are dispatched in
+// index order, so with many more (sequence, kv-head) pairs than the device
+// holds at once, a long sequence reached late leaves a tail of one long
+// workgroup per compute unit; taking sequences longest first fills that
+// tail with short ones.  Workgroup x takes the sequence of rank x / Hkv in
+// the order (16-token units descending, index ascending), found by a radix
+// selection the workgroup runs on its own: a histogram of the units names
+// the rank's length class, a count over the sequence indices its member.
+// The order is a permutation of the batch, the same in every workgroup;
+// results do not depend on it.  At most kLptMaxSeqs sequences (four per
+// thread of a 256-thread workgroup).
+constexpr int kLptMaxSeqs = 1024;
+constexpr int kLptBins = 1024;
+
+// inclusive prefix sum over the workgroup's 256 threads (one value each)
+template <int WAVES>
+__device__ __forceinline__ int block_incl_scan_i(int x, int* s_wave) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    x = wave_incl_scan_i(x);
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int v = 0; v < WAVES - 1; ++v)
+        if (v < w) before += s_wave[v];
+    return x + before;
+}
+
+template <int WAVES>
+__device__ __forceinline__ int lpt_sequence(const DecodeArgs& a, int rank, int* s_tmp, int* s_pick) {
+    static_assert(WAVES * 64 * 4 == kLptMaxSeqs && kLptBins == kLptMaxSeqs, "four items per thread");
+    const int tid = threadIdx.x;
+    const int B = a.num_seqs;
+    int* s_hist = s_tmp;                 // [kLptBins]
+    int* s_wave = s_tmp + kLptBins;      // [WAVES] per scan
+    // this thread's sequences 4 tid .. 4 tid + 3 and their classes
+    // (0 = longest; an index past the batch has none)
+    int cls[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 4 * tid + k;
+        const int u = i < B ? (a.seq_lens[i] + kBS - 1) / kBS : -1;
+        cls[k] = u < 0 ? -1 : kLptBins - 1 - min(u, kLptBins - 1);
+        s_hist[4 * tid + k] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (cls[k] >= 0) atomicAdd(&s_hist[cls[k]], 1);
+    __syncthreads();
+    // classes 4 tid .. 4 tid + 3: the first whose running count passes rank
+    int c[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        c[k] = s_hist[4 * tid + k];
+        sum += c[k];
+    }
+    int run = block_incl_scan_i<WAVES>(sum, s_wave) - sum;   // sequences in classes before 4 tid
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (run <= rank && rank < run + c[k]) {
+            s_pick[0] = 4 * tid + k;   // the class
+            s_pick[1] = rank - run;    // the member's place in it
+        }
+        run += c[k];
+    }
+    __syncthreads();
+    const int K = s_pick[0], m = s_pick[1];
+    // the m-th sequence of class K in index order
+    int f[4], fsum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[k] = cls[k] == K;
+        fsum += f[k];
+    }
+    int before = block_incl_scan_i<WAVES>(fsum, s_wave + WAVES) - fsum;
+    __syncthreads();   // every thread has read s_pick
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (f[k] && before == m) s_pick[2] = 4 * tid + k;
+        before += f[k];
+    }
+    __syncthreads();
+    return s_pick[2];
+}
+
 // One workgroup per (sequence, kv-head, partition): the one-pass mode
 // (SPLIT = false, one partition) and the fixed-size split-KV mode.
 template <int D, int KIND, int BS, bool SPLIT, bool MQ, int WAVES>
@@ -461,7 +559,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
     __shared__ float smem[combine_floats<D, KIND, WAVES>()];
     const int Hkv = a.num_kv_heads;
     const int h = blockIdx.x % Hkv;
-    const int b = blockIdx.x / Hkv;
+    int b = blockIdx.x / Hkv;
+    if constexpr (!SPLIT) {
+        if (a.lpt_order) {   // uniform
+            static_assert(combine_floats<D, KIND, WAVES>() >= kLptBins + 2 * WAVES, "LDS for the selection");
+            __shared__ int s_pick[3];
+            b = lpt_sequence<WAVES>(a, b, reinterpret_cast<int*>(smem), s_pick);
+        }
+    }
     const int part = blockIdx.y;
     const int L = a.seq_lens[b];
     const int nblk = (L + kBS - 1) / kBS;
@@ -494,18 +599,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const DecodeArgs a) 
 // and the first piece's workgroup of kv-head 0 records (first slot, count)
 // for the merge.  The partials are staged in LDS and stored at the end.
 // ---------------------------------------------------------------------------
-// inclusive prefix sum over the wave's 64 lanes: DPP row shifts within each
-// 16-lane row, then row broadcasts carry the row totals upward (no LDS)
-__device__ __forceinline__ int wave_incl_scan_i(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-    return x;
-}
-
 // the split that owns unit x: the largest s with floor(s * W / S) <= x
 __device__ __forceinline__ int owner(long long x, long long W, int S) {
     return (int)(((x + 1) * S - 1) / W);
@@ -655,11 +748,20 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KIND
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;
 
+// one-pass mode: longest sequences first when the grid is several times
+// what the device holds (below that the order hardly matters)
+#ifndef PA_LPT_MIN_WORKGROUPS
+#define PA_LPT_MIN_WORKGROUPS 1024
+#endif
+
 template <int D, int KIND, int BS, bool SPLIT, bool MQ>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), SPLIT ? (unsigned)a.grid_parts : 1u);
+    DecodeArgs k = a;
+    k.lpt_order = !SPLIT && kWaves == 4 && a.num_seqs <= kLptMaxSeqs &&
+                  (long long)a.num_seqs * a.num_kv_heads >= PA_LPT_MIN_WORKGROUPS;
     hipLaunchKernelGGL((decode_kernel<D, KIND, BS, SPLIT, MQ, kWaves>), grid,
-                       dim3(64 * kWaves), 0, s, a);
+                       dim3(64 * kWaves), 0, s, k);
     return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct DecodeArgs {
     int grid_parts;       // partitions in the grid (1 in one-pass mode); balanced: splits per kv-head
     int balanced;         // balanced split-KV: grid (splits, kv-heads), partials by piece slot
     void* piece_info;     // balanced: int2 [num_seqs] = (first piece slot, piece count)
+    int lpt_order;        // one-pass: workgroups take sequences longest first (set at launch)
     float scale;
 };
 
