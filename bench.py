@@ -283,27 +283,64 @@ def time_mixed(torch, pa, dd, dp, m, P, steps, warmup, flush):
             [t.ms(i, 1, 2) for i in range(steps)])
 
 
-def mixed_summary(m, P, step, dec, pre):
+def time_mixed_one_call(torch, pa, dd, dp, m, P, steps, warmup, flush):
+    """The mixed step through pa_mixed_step (the decode rows' merge inside
+    the chunks' launch): one flush, one call, between one pair of events."""
+    dec, pre = m.decode, m.prefill
+    out_d = torch.empty_like(dd.q)
+    out_p = torch.empty_like(dp.q)
+    ws = torch.empty(max(pa.decode_workspace_size(dec.num_seqs, dec.num_q_heads, dec.head_dim,
+                                                  dec.max_seq_len, P), 256),
+                     dtype=torch.uint8, device="cuda")
+
+    def launch(ev):
+        ev[0].record()
+        pa.mixed_step(dd.q, dd.bt, dd.sl, dp.q, dp.cu, dp.bt, dp.sl, dd.k, dd.v,
+                      max_seq_len=dec.max_seq_len, max_q_len=pre.max_q_len, partition_size=P,
+                      scale=dec.scale, dec_out=out_d, pre_out=out_p, workspace=ws)
+        ev[1].record()
+
+    wt = Timer(torch, warmup, 2)
+    for i in range(warmup):
+        flush()
+        launch(wt.ev[i])
+    torch.cuda.synchronize()
+    t = Timer(torch, steps, 2)
+    for i in range(steps):
+        flush()
+        launch(t.ev[i])
+    torch.cuda.synchronize()
+    return [t.ms(i, 0, 1) for i in range(steps)]
+
+
+def mixed_summary(m, P, one_call, step, dec, pre):
     mean = lambda xs: sum(xs) / len(xs)
     sm, dm, pm = mean(step), mean(dec), mean(pre)
+    om = mean(one_call)
     tflops = m.prefill.flops() / pm / 1e9
     attended = m.decode.total_tokens + m.prefill.pairs()
     return {
         "workload": "mixed step: 16 decode seqs (1024-8192) + 4 chunks of 512 over a 2048-token "
                     "shared prefix, 32/8 heads, d=128, bf16, seed 4",
         "decode_partition_size": P,
-        "step_ms": round(sm, 5),
-        "p10_ms": round(sorted(step)[len(step) // 10], 5),
-        "p90_ms": round(sorted(step)[(9 * len(step)) // 10], 5),
-        "tokens_attended_per_s": round(attended / sm * 1e3, 1),
-        "note": "one flush, then pa_decode and pa_prefill_chunk back to back on one stream "
-                "between one pair of HIP events; the parts split at an event between them",
-        "decode": {"ms": round(dm, 5), "kv_bytes": m.decode.kv_bytes(),
-                   "kv_GBps": round(m.decode.kv_bytes() / dm / 1e6, 2),
-                   "pct_hbm_peak": round(100 * m.decode.kv_bytes() / dm / 1e6 / HBM_PEAK_GBS, 2)},
-        "prefill": {"ms": round(pm, 5), "TFLOPs": round(tflops, 2),
-                    "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
-                    "pairs": m.prefill.pairs(), "flops": m.prefill.flops()},
+        "step_ms": round(om, 5),
+        "p10_ms": round(sorted(one_call)[len(one_call) // 10], 5),
+        "p90_ms": round(sorted(one_call)[(9 * len(one_call)) // 10], 5),
+        "tokens_attended_per_s": round(attended / om * 1e3, 1),
+        "note": "step: one flush, then one pa_mixed_step call (decode rows' attention, then the "
+                "chunks with the decode rows' merge in their launch) between one pair of HIP "
+                "events; two_calls: pa_decode and pa_prefill_chunk back to back on one stream, "
+                "split at an event between them",
+        "two_calls": {
+            "step_ms": round(sm, 5),
+            "decode": {"ms": round(dm, 5), "kv_bytes": m.decode.kv_bytes(),
+                       "kv_GBps": round(m.decode.kv_bytes() / dm / 1e6, 2),
+                       "pct_hbm_peak": round(100 * m.decode.kv_bytes() / dm / 1e6 / HBM_PEAK_GBS,
+                                             2)},
+            "prefill": {"ms": round(pm, 5), "TFLOPs": round(tflops, 2),
+                        "pct_bf16_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+                        "pairs": m.prefill.pairs(), "flops": m.prefill.flops()},
+        },
     }
 
 
@@ -554,9 +591,11 @@ def profile_one(args, W):
     if n == 4:
         m = W.config4(pad=0, partition_size=args.partition_size)
         dd, dp = mixed_devices(m)
+        one = time_mixed_one_call(torch, pa, dd, dp, m, args.partition_size, args.steps,
+                                  args.warmup, flush)
         step, dec, pre = time_mixed(torch, pa, dd, dp, m, args.partition_size, args.steps,
                                     args.warmup, flush)
-        res.update(mixed_summary(m, args.partition_size, step, dec, pre))
+        res.update(mixed_summary(m, args.partition_size, one, step, dec, pre))
     else:
         w = W.config3(pad=0) if n == 3 else W.config5(pad=0, partition_size=args.partition_size)
         dd = Dev(w)
@@ -636,8 +675,9 @@ def main():
         # the mixed step, timed as one step (decode rows balanced across the chip)
         m = W.config4(pad=0, partition_size=-1)
         dd, dp = mixed_devices(m)
+        one = time_mixed_one_call(torch, pa, dd, dp, m, -1, 20, 3, flush)
         step, dec, pre = time_mixed(torch, pa, dd, dp, m, -1, 20, 3, flush)
-        per_config["C4"] = mixed_summary(m, -1, step, dec, pre)
+        per_config["C4"] = mixed_summary(m, -1, one, step, dec, pre)
         del dd, dp
         per_config["kv_write"] = [time_write(torch, pa, wl, 20, 3, flush) for wl in write_cases(W)]
         per_config["verify"] = time_verify(torch, pa, W, 20, 3, flush, args.partition_size)

@@ -360,6 +360,35 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
                      const float* v_scale, void* stream);
 
 /*
+ * One mixed serving step: decode rows and prefill chunks over one KV cache,
+ * the way the pages' engine runs chunked prefill beside decoding sequences
+ * (vllm-metis 0.1.0, "How the model maps onto vLLM").  The result is that of
+ * pa_decode on the decode part (dec_*, num_seqs, max_seq_len,
+ * partition_size, workspace: as there) followed by pa_prefill_chunk on the
+ * chunk part (pre_*, cu_q_lens, total_q, max_q_len, num_chunks: as there),
+ * bit for bit; the shared arguments (dtypes, caches, head counts, head_dim,
+ * block size, pool size, scale, fp8 scales) describe both.  When the decode
+ * rows need a split-KV merge, it runs inside the chunks' launch, ahead of
+ * each workgroup's own rows, instead of as a launch of its own: two launches
+ * per step instead of three (a merge over 32 or more fixed partitions, which
+ * takes a workgroup per row, keeps its own launch).  Every argument of both parts is validated
+ * before anything is enqueued; either part may be empty (num_seqs == 0, or
+ * num_chunks == 0 / max_q_len == 0).  The workspace must not overlap any
+ * output.
+ */
+int pa_mixed_step(void* dec_out, const void* dec_q, const int32_t* dec_block_table,
+                  int dec_max_blocks_per_seq, const int32_t* dec_seq_lens, int num_seqs,
+                  int max_seq_len, int partition_size, void* workspace, size_t workspace_bytes,
+                  void* pre_out, float* pre_out_lse, const void* pre_q,
+                  const int32_t* cu_q_lens, int total_q, int max_q_len,
+                  const int32_t* pre_block_table, int pre_max_blocks_per_seq,
+                  const int32_t* pre_seq_lens, int num_chunks,
+                  int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                  void* stream);
+
+/*
  * Cache write: store the K/V rows of num_tokens new tokens into their cache
  * slots, the step that precedes attention in every decode step and prefill
  * chunk (the cache is addressed by (block, offset) through block tables:

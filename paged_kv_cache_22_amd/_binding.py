@@ -43,6 +43,9 @@ SIGNATURES = {
                               _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "pa_write_kv": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp,
                          _vp]),
+    "pa_mixed_step": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _vp, _sz,
+                           _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _i,
+                           _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
 }
 
 
@@ -348,6 +351,50 @@ def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_table, seq_lens, *, max_
                               _dev(v_scale, "v_scale"), _stream(q))
     _check("pa_prefill_chunk", st)
     return (out, out_lse) if want_lse else out
+
+
+def mixed_step(dec_q, dec_block_table, dec_seq_lens, pre_q, cu_q_lens, pre_block_table,
+               pre_seq_lens, k_cache, v_cache, *, max_seq_len: int, max_q_len: int,
+               partition_size: int = PA_PARTITION_BALANCED, scale: Optional[float] = None,
+               k_scale=None, v_scale=None, dec_out=None, pre_out=None, pre_out_lse=None,
+               want_lse: bool = False, workspace=None):
+    """One mixed step (pa_mixed_step): decode rows dec_q [B, Hq, d] and
+    prefill chunks pre_q [total_q, Hq, d] over one cache, with the decode
+    rows' merge inside the chunks' launch.  Returns (dec_out, pre_out), plus
+    the chunks' lse when want_lse."""
+    torch = _torch()
+    B, Hq, d, NB, Hkv, bs = _kv_dims(dec_q, k_cache, v_cache)
+    total_q, Hq_p, d_p = pre_q.shape
+    if (Hq_p, d_p) != (Hq, d):
+        raise ValueError("pre_q must have dec_q's heads and head_dim")
+    if pre_q.dtype != dec_q.dtype:
+        raise ValueError("pre_q and dec_q must have one dtype")
+    if dec_out is None:
+        dec_out = torch.empty_like(dec_q)
+    if pre_out is None:
+        pre_out = torch.empty_like(pre_q)
+    if want_lse and pre_out_lse is None:
+        pre_out_lse = torch.empty((total_q, Hq), dtype=torch.float32, device=pre_q.device)
+    if scale is None:
+        scale = d ** -0.5
+    ws_need = decode_workspace_size(B, Hq, d, max_seq_len, partition_size)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dec_q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_mixed_step(_dev(dec_out, "dec_out"), _dev(dec_q, "dec_q"),
+                           _dev(dec_block_table, "dec_block_table"), dec_block_table.shape[1],
+                           _dev(dec_seq_lens, "dec_seq_lens"), B, int(max_seq_len),
+                           int(partition_size), _dev(workspace, "workspace"), ws_bytes,
+                           _dev(pre_out, "pre_out"), _dev(pre_out_lse, "pre_out_lse"),
+                           _dev(pre_q, "pre_q"), _dev(cu_q_lens, "cu_q_lens"), total_q,
+                           int(max_q_len), _dev(pre_block_table, "pre_block_table"),
+                           pre_block_table.shape[1], _dev(pre_seq_lens, "pre_seq_lens"),
+                           pre_seq_lens.shape[0], _dtype_code(dec_q, False),
+                           _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dtype_code(k_cache, True), Hq, Hkv, d, bs, NB, float(scale),
+                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(dec_q))
+    _check("pa_mixed_step", st)
+    return (dec_out, pre_out, pre_out_lse) if want_lse else (dec_out, pre_out)
 
 
 def _rows(t, name: str):

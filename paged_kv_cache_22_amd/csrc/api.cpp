@@ -239,7 +239,10 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
                 int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, int block_size, float scale, const float* k_scale,
                 const float* v_scale, int partition_size, int max_seq_len, void* workspace,
-                size_t workspace_bytes, void* stream, int stages = PA_STAGE_ALL) {
+                size_t workspace_bytes, void* stream, int stages = PA_STAGE_ALL,
+                pa::MergeArgs* deferred = nullptr) {
+    // deferred: the merge is not launched but described there (its out left
+    // NULL when none is due), for a later launch to run
     const bool run_attn = stages & PA_STAGE_ATTENTION, run_merge = stages & PA_STAGE_MERGE;
     const int rows_per_seq = q_len * num_q_heads;   // output rows of one sequence
     pa::DecodeArgs a = make_decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_table,
@@ -289,6 +292,10 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
         m.piece_slots = (int)slots;
         m.q_len = q_len;
         m.num_kv_heads = num_kv_heads;
+        if (deferred) {
+            *deferred = m;
+            return PA_OK;
+        }
         return hip_status(pa::launch_merge(m, stream));
     }
     const int parts = (int)(((long long)max_seq_len + partition_size - 1) / partition_size);
@@ -324,7 +331,56 @@ int decode_impl(void* out, const void* q, int q_dtype, int q_len, const void* k_
     m.num_q_heads = rows_per_seq;
     m.head_dim = head_dim;
     m.skip_single = 1;
+    if (deferred) {
+        *deferred = m;
+        return PA_OK;
+    }
     return hip_status(pa::launch_merge(m, stream));
+}
+
+// pa_prefill_chunk's checks and kernel arguments; *empty: nothing to launch
+int prefill_prepare(void* out, float* out_lse, const void* q, int q_dtype, const int32_t* cu_q_lens,
+                    int total_q, int max_q_len, const void* k_cache, const void* v_cache,
+                    int kv_dtype, const int32_t* block_table, int max_blocks_per_seq,
+                    const int32_t* seq_lens, int num_chunks, int num_q_heads, int num_kv_heads,
+                    int head_dim, int block_size, int num_blocks, float scale,
+                    const float* k_scale, const float* v_scale, pa::PrefillArgs& a, bool* empty) {
+    *empty = num_chunks == 0 || max_q_len == 0;
+    int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
+                           seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           scale, k_scale, v_scale, *empty);
+    if (st != PA_OK) return st;
+    if (!*empty && (!out || !cu_q_lens)) return PA_ERR_NULL;
+    if (!aligned16(out) || (reinterpret_cast<uintptr_t>(cu_q_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(out_lse) & 3u))
+        return PA_ERR_ALIGN;
+    if (num_chunks < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_SHAPE;
+    if ((long long)num_chunks * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const long long groups = ((long long)max_q_len * (num_q_heads / num_kv_heads) + 31) / 32;
+    if (groups > kMaxGridY) return PA_ERR_UNSUPPORTED;
+    a = pa::PrefillArgs{};
+    a.out = out;
+    a.out_lse = out_lse;
+    a.q = q;
+    a.cu_q_lens = cu_q_lens;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
+    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.num_chunks = num_chunks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale = scale;
+    return PA_OK;
 }
 
 }  // namespace
@@ -578,42 +634,61 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype, cons
                      const int32_t* seq_lens, int num_chunks, int num_q_heads, int num_kv_heads,
                      int head_dim, int block_size, int num_blocks, float scale, const float* k_scale,
                      const float* v_scale, void* stream) {
-    const bool empty = num_chunks == 0 || max_q_len == 0;
-    int st = common_checks(q, k_cache, v_cache, q_dtype, kv_dtype, block_table, max_blocks_per_seq,
-                           seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                           scale, k_scale, v_scale, empty);
+    pa::PrefillArgs a;
+    bool empty;
+    const int st = prefill_prepare(out, out_lse, q, q_dtype, cu_q_lens, total_q, max_q_len, k_cache,
+                                   v_cache, kv_dtype, block_table, max_blocks_per_seq, seq_lens,
+                                   num_chunks, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   num_blocks, scale, k_scale, v_scale, a, &empty);
+    if (st != PA_OK || empty) return st;
+    return hip_status(pa::launch_prefill(a, stream));
+}
+
+int pa_mixed_step(void* dec_out, const void* dec_q, const int32_t* dec_block_table,
+                  int dec_max_blocks_per_seq, const int32_t* dec_seq_lens, int num_seqs,
+                  int max_seq_len, int partition_size, void* workspace, size_t workspace_bytes,
+                  void* pre_out, float* pre_out_lse, const void* pre_q, const int32_t* cu_q_lens,
+                  int total_q, int max_q_len, const int32_t* pre_block_table,
+                  int pre_max_blocks_per_seq, const int32_t* pre_seq_lens, int num_chunks,
+                  int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  float scale, const float* k_scale, const float* v_scale, void* stream) {
+    // every argument of both parts is checked before anything is enqueued
+    int st = decode_checks(dec_q, q_dtype, k_cache, v_cache, kv_dtype, dec_block_table,
+                           dec_max_blocks_per_seq, dec_seq_lens, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
+                           v_scale, partition_size, max_seq_len);
     if (st != PA_OK) return st;
-    if (!empty && (!out || !cu_q_lens)) return PA_ERR_NULL;
-    if (!aligned16(out) || (reinterpret_cast<uintptr_t>(cu_q_lens) & 3u) ||
-        (reinterpret_cast<uintptr_t>(out_lse) & 3u))
-        return PA_ERR_ALIGN;
-    if (num_chunks < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_SHAPE;
-    if ((long long)num_chunks * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
-    const long long groups = ((long long)max_q_len * (num_q_heads / num_kv_heads) + 31) / 32;
-    if (groups > kMaxGridY) return PA_ERR_UNSUPPORTED;
-    if (num_chunks == 0 || max_q_len == 0) return PA_OK;
-    pa::PrefillArgs a{};
-    a.out = out;
-    a.out_lse = out_lse;
-    a.q = q;
-    a.cu_q_lens = cu_q_lens;
-    a.total_q = total_q;
-    a.max_q_len = max_q_len;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_table = block_table;
-    a.seq_lens = seq_lens;
-    a.k_scale = kv_dtype == PA_FP8_E4M3 ? k_scale : nullptr;
-    a.v_scale = kv_dtype == PA_FP8_E4M3 ? v_scale : nullptr;
-    a.q_dtype = q_dtype;
-    a.kv_dtype = kv_dtype;
-    a.num_chunks = num_chunks;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.head_dim = head_dim;
-    a.block_size = block_size;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.scale = scale;
+    if (num_seqs > 0 && !dec_out) return PA_ERR_NULL;
+    if (!aligned16(dec_out)) return PA_ERR_ALIGN;
+    if ((long long)num_seqs * num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    pa::PrefillArgs a;
+    bool empty;
+    st = prefill_prepare(pre_out, pre_out_lse, pre_q, q_dtype, cu_q_lens, total_q, max_q_len,
+                         k_cache, v_cache, kv_dtype, pre_block_table, pre_max_blocks_per_seq,
+                         pre_seq_lens, num_chunks, num_q_heads, num_kv_heads, head_dim, block_size,
+                         num_blocks, scale, k_scale, v_scale, a, &empty);
+    if (st != PA_OK) return st;
+    // the decode rows' attention (the workspace is checked there, before any
+    // launch); their merge, when one is due, goes into the chunks' launch
+    // (or runs on its own when there are no chunks)
+    pa::MergeArgs m{};
+    st = decode_impl(dec_out, dec_q, q_dtype, 1, k_cache, v_cache, kv_dtype, dec_block_table,
+                     dec_max_blocks_per_seq, dec_seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, scale, k_scale, v_scale, partition_size, max_seq_len,
+                     workspace, workspace_bytes, stream, PA_STAGE_ALL, &m);
+    if (st != PA_OK) return st;
+    const bool merge_due = m.out != nullptr;
+    if (merge_due && (empty || !pa::merge_fusable(m))) {
+        // no chunks to carry it, or a merge of many partitions (a workgroup
+        // per row): a launch of its own, as pa_decode makes it
+        st = hip_status(pa::launch_merge(m, stream));
+        if (st != PA_OK || empty) return st;
+    } else if (merge_due) {
+        a.merge = m;
+        a.merge_rows = num_seqs * num_q_heads;
+    }
+    if (empty) return PA_OK;
     return hip_status(pa::launch_prefill(a, stream));
 }
 

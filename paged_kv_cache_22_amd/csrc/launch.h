@@ -84,6 +84,11 @@ struct PrefillArgs {
     int part_stride;
     int max_blocks_per_seq;
     float scale;
+    // merge_rows > 0: before its own rows, the kernel merges rows 0 ..
+    // merge_rows - 1 of a decode step's split-KV partials described by merge
+    // (same head_dim and output dtype), one wave per row (a mixed step)
+    int merge_rows;
+    MergeArgs merge;
 };
 
 struct WriteArgs {
@@ -120,6 +125,9 @@ int static_workspace(void** ptr, size_t* bytes);
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
+// whether launch_merge would merge a's rows with one wave per row (the form
+// a prefill launch can run ahead of its own rows, bit for bit the same)
+bool merge_fusable(const MergeArgs& a);
 int launch_write_kv(const WriteArgs& a, void* stream);
 
 }  // namespace pa

@@ -58,8 +58,14 @@ int launch_merge(const MergeArgs& a, void*) {
     return a.num_seqs > 0 && a.num_q_heads > 0 ? 0 : 1;
 }
 
+bool merge_fusable(const MergeArgs& a) { return a.piece_info || a.max_parts < 32; }
+
 int launch_prefill(const PrefillArgs& a, void*) {
     ++g_launches;
+    // a mixed step's merge rows: every decode row, of the prefill's head_dim
+    if (a.merge_rows > 0 && ((long long)a.merge.num_seqs * a.merge.num_q_heads != a.merge_rows ||
+                             a.merge.head_dim != a.head_dim))
+        return 1;
     if (a.part_out) {
         const size_t n = (size_t)a.total_q * a.num_q_heads * a.part_stride;
         touch(a.part_out, n * a.head_dim * sizeof(float));
@@ -192,6 +198,30 @@ int main() {
     EXPECT(pa_write_kv(fake(1), fake(2), PA_FP8_E4M3, fake(3), fake(4), PA_BF16, 2048, 2048,
                        ifake(5), 64, 8, 128, 16, 10000, ffake(6), ffake(7), nullptr) == PA_OK);
 
+    // the mixed step: workspaces of exactly the queried size, both modes,
+    // either part empty
+    for (int P : {PA_PARTITION_BALANCED, 512, 0}) {
+        const size_t need = pa_decode_workspace_size(16, 32, 128, 8192, P);
+        Workspace ws(need);
+        EXPECT(pa_mixed_step(fake(1), fake(2), ifake(3), 512, ifake(4), 16, 8192, P, ws.p, need,
+                             fake(5), nullptr, fake(6), ifake(7), 2048, 512, ifake(8), 160,
+                             ifake(9), 4, PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128, 16,
+                             100000, 0.088f, nullptr, nullptr, nullptr) == PA_OK);
+        EXPECT(pa_mixed_step(fake(1), fake(2), ifake(3), 512, ifake(4), 16, 8192, P, ws.p, need,
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 160, nullptr, 0,
+                             PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128, 16, 100000, 0.088f,
+                             nullptr, nullptr, nullptr) == PA_OK);
+        EXPECT(pa_mixed_step(nullptr, nullptr, nullptr, 512, nullptr, 0, 0, P, nullptr, 0,
+                             fake(5), nullptr, fake(6), ifake(7), 2048, 512, ifake(8), 160,
+                             ifake(9), 4, PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128, 16,
+                             100000, 0.088f, nullptr, nullptr, nullptr) == PA_OK);
+        if (need > 0)
+            EXPECT(pa_mixed_step(fake(1), fake(2), ifake(3), 512, ifake(4), 16, 8192, P, ws.p,
+                                 need - 1, fake(5), nullptr, fake(6), ifake(7), 2048, 512, ifake(8),
+                                 160, ifake(9), 4, PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128,
+                                 16, 100000, 0.088f, nullptr, nullptr, nullptr) == PA_ERR_WORKSPACE);
+    }
+
     // extreme sizes are refused, not overflowed
     const int big = 0x7fffffff;
     EXPECT(decode(big, 32, 8, 128, 16, 512, 4096, nullptr, 0) != PA_OK);
@@ -206,6 +236,10 @@ int main() {
                             nullptr, nullptr, nullptr) != PA_OK);
     EXPECT(pa_write_kv(fake(1), fake(2), PA_BF16, fake(3), fake(4), PA_BF16, big, big, ifake(5), big,
                        big, 128, 16, big, nullptr, nullptr, nullptr) != PA_OK);
+    EXPECT(pa_mixed_step(fake(1), fake(2), ifake(3), 512, ifake(4), big, 8192, PA_PARTITION_BALANCED,
+                         nullptr, 0, fake(5), nullptr, fake(6), ifake(7), big, big, ifake(8), 160,
+                         ifake(9), big, PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128, 16,
+                         100000, 0.088f, nullptr, nullptr, nullptr) != PA_OK);
     EXPECT(pa_decode_shared_prefix_workspace_size(big, big, big, 1, 128, big, big, 16) == 0);
     EXPECT(pa_decode_shared_prefix_workspace_size(64, 1, 32, 8, 128, big, 4096, 1024) > 0);
 

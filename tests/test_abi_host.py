@@ -286,3 +286,32 @@ def test_noalloc_buffer_size_matches_header():
     assert pa.decode_workspace_size(2, 32, 128, 65536, 16) > B.STATIC_WORKSPACE_BYTES
     assert pa.decode_workspace_size(3100, 32, 128, 4096, -1) > B.STATIC_WORKSPACE_BYTES
     assert pa.decode_workspace_size(64, 32, 128, 4096, -1) < B.STATIC_WORKSPACE_BYTES
+
+
+def mixed_call(**over):
+    a = dict(dout=P, dq=P, dbt=P, dmb=256, dsl=P, B=16, max_len=4096, part=-1, ws=P, wsb=1 << 30,
+             pout=P, plse=None, pq=P, cu=P, tq=2048, mq=512, pbt=P, pmb=160, psl=P, nc=4,
+             qd=1, k=P, v=P, kvd=1, hq=32, hkv=8, d=128, bs=16, nb=9000, scale=0.088, ks=None,
+             vs=None, stream=None)
+    a.update(over)
+    return pa.lib.pa_mixed_step(*a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dout=None), NULL), (dict(pout=None), NULL), (dict(cu=None), NULL),
+    (dict(dsl=None), NULL), (dict(psl=None), NULL), (dict(kvd=2), NULL),   # fp8 without scales
+    (dict(qd=0), DTYPE), (dict(d=96), UNSUP), (dict(bs=24), UNSUP), (dict(part=24), UNSUP),
+    (dict(dout=P + 8), ALIGN), (dict(pout=P + 8), ALIGN), (dict(plse=P + 2), ALIGN),
+    (dict(ws=P + 16), ALIGN), (dict(part=-1, ws=None), WS), (dict(part=512, wsb=100), WS),
+    (dict(mq=-1), SHAPE), (dict(max_len=5000), SHAPE), (dict(scale=0.0), SHAPE),
+    (dict(hq=30), SHAPE),
+])
+def test_mixed_step_rejects_before_launch(over, status):
+    """Every argument of both parts is checked before anything is enqueued."""
+    assert mixed_call(**over) == status
+
+
+def test_mixed_step_empty_accepts_null_arrays():
+    assert mixed_call(B=0, dout=None, dq=None, dbt=None, dsl=None, max_len=0, ws=None, wsb=0,
+                      nc=0, mq=0, tq=0, pout=None, pq=None, cu=None, pbt=None, psl=None) == OK
+    assert mixed_call(B=0, dout=None, dq=None, nc=0, mq=0, d=96) == UNSUP   # sizes still checked

@@ -7,7 +7,8 @@ library's calls enqueue kernels only -- no allocation, no memset, no host
 read of device data -- so they can be captured.  Here one step is captured
 once: the cache write of each sequence's newest token, decode in the
 balanced mode, at 512-token partitions and at 128-token partitions (up to
-24 per sequence: the streamed kernel), and a causal prefill chunk.  Its
+24 per sequence: the streamed kernel), a causal prefill chunk, and a mixed
+step (decode rows and chunks in one call).  Its
 inputs (q, the new K/V rows and their slots, the sequence lengths) are then
 rewritten in place and the graph replayed several times, with eager work
 and synchronisations between the replays; every replay must equal, bit for
@@ -50,6 +51,12 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
                          dtype=torch.uint8, device="cuda") for P in MODES}
     outs = {P: torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda") for P in MODES}
     pout = torch.empty_like(pq)
+    # a mixed step over the decode cache: the decode rows (balanced) and the
+    # chunks, their tables naming blocks of the decode pool
+    mbt = dev(np.random.default_rng(413).integers(0, wl.num_blocks, size=pw.block_table.shape)
+              .astype(np.int32))
+    mws = torch.empty_like(ws[BAL])
+    m_dec, m_pre = torch.empty_like(outs[BAL]), torch.empty_like(pq)
 
     def step():
         pa.write_kv(new_k, new_v, k, v, slots)
@@ -58,6 +65,9 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
                       out=outs[P], workspace=ws[P])
         pa.prefill_chunk(pq, pcu, pk, pv, pbt, psl, max_q_len=int(pw.max_q_len), scale=pw.scale,
                          out=pout)
+        pa.mixed_step(q, bt, lens, pq, pcu, mbt, psl, k, v, max_seq_len=max_len,
+                      max_q_len=int(pw.max_q_len), partition_size=BAL, scale=wl.scale,
+                      dec_out=m_dec, pre_out=m_pre, workspace=mws)
 
     rng = np.random.default_rng(412)
 
@@ -94,6 +104,7 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
         torch.cuda.synchronize()
         got = {P: outs[P].clone() for P in outs}
         got_p = pout.clone()
+        got_m = (m_dec.clone(), m_pre.clone())
         k_after, v_after = k.clone(), v.clone()
         # the same calls eagerly, on the same inputs and the same starting cache
         k.copy_(k0)
@@ -104,6 +115,10 @@ def test_step_captured_in_a_graph_replays_like_eager_calls():
         for P in outs:
             assert torch.equal(got[P].view(torch.int16), outs[P].view(torch.int16)), (rep, P)
         assert torch.equal(got_p.view(torch.int16), pout.view(torch.int16)), rep
+        assert torch.equal(got_m[0].view(torch.int16), m_dec.view(torch.int16)), rep
+        assert torch.equal(got_m[1].view(torch.int16), m_pre.view(torch.int16)), rep
+        # the mixed step's decode rows are pa_decode's, bit for bit
+        assert torch.equal(got_m[0].view(torch.int16), got[BAL].view(torch.int16)), rep
         assert torch.equal(k_after.view(torch.int16), k.view(torch.int16)), rep
         assert torch.equal(v_after.view(torch.int16), v.view(torch.int16)), rep
         # and the oracle, on the cache as the step left it
