@@ -69,7 +69,7 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 template <int D, int KIND, int BS, int NC>
-__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
+__device__ __forceinline__ void prefill_rows(const PrefillArgs& a) {
     using T = Tile<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int NT = T::NT;
@@ -95,25 +95,6 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
     // wave index: uniform, and known to be below kWaves (which folds the
     // copy bookkeeping below into constants where the wave does not matter)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & (kWaves - 1);
-    if (a.merge_rows > 0) {
-        // A mixed step's decode rows: their split-KV partials (written by the
-        // decode kernel launched before this one) merged here, before the
-        // workgroup's own work, so the merge needs no launch of its own.
-        // The rows go to the workgroups of the first half of the grid's row
-        // tiles (all of them when there is one): causal tiles early in a
-        // chunk see fewer keys, and those workgroups finish before the
-        // others even with the merge's round trips added.  Row r: wave
-        // r / n of eligible workgroup r % n.
-        const unsigned yh = gridDim.y / 2;
-        if (yh == 0 || blockIdx.y < yh) {
-            const unsigned ny = yh ? yh : gridDim.y;
-            const unsigned n = gridDim.x * ny * gridDim.z;
-            const unsigned wg = blockIdx.x + gridDim.x * (blockIdx.y + ny * blockIdx.z);
-            const int hq = a.merge.num_q_heads;
-            for (long long r = wg + (long long)n * w; r < a.merge_rows; r += (long long)n * kWaves)
-                merge_row<D, KIND != KV_F32>(a.merge, (int)(r / hq), (int)(r % hq), lane);
-        }
-    }
     const int r = lane & 15, c = lane >> 4;
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads, G = Hq / Hkv;
     const int h = blockIdx.x % Hkv;
@@ -409,6 +390,30 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs 
             store4(o + 16 * n + 4 * c, acc[ct][n][0] * inv, acc[ct][n][1] * inv,
                    acc[ct][n][2] * inv, acc[ct][n][3] * inv);
         if (a.out_lse && c == 0) a.out_lse[qrow_idx[ct]] = (m[ct] * C + fast_log2(lsum)) * kLn2;
+    }
+}
+
+// The workgroup's rows, then (a mixed step) its share of the decode rows'
+// split-KV merge: the partials were written by the decode kernel launched
+// before this one, and the merge needs no launch of its own.  The merge rows
+// go to the workgroups of the first half of the grid's row tiles (all of
+// them when there is one), the causal tiles that see the fewest keys; a
+// wave merges its rows as soon as its own are done.  Row r: wave r / n of
+// eligible workgroup r % n.
+template <int D, int KIND, int BS, int NC>
+__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(const PrefillArgs a) {
+    prefill_rows<D, KIND, BS, NC>(a);
+    if (a.merge_rows > 0) {
+        const unsigned yh = gridDim.y / 2;
+        if (yh == 0 || blockIdx.y < yh) {
+            const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            const unsigned ny = yh ? yh : gridDim.y;
+            const unsigned n = gridDim.x * ny * gridDim.z;
+            const unsigned wg = blockIdx.x + gridDim.x * (blockIdx.y + ny * blockIdx.z);
+            const int hq = a.merge.num_q_heads;
+            for (long long r = wg + (long long)n * w; r < a.merge_rows; r += (long long)n * kWaves)
+                merge_row<D, KIND != KV_F32>(a.merge, (int)(r / hq), (int)(r % hq), threadIdx.x & 63);
+        }
     }
 }
 
