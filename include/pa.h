@@ -54,9 +54,7 @@
  *
  * Supported: head_dim 64 or 128; block_size 16, 32 or 64 (vllm-mblt 0.8.0,
  * "Chunked Prefill Auto-Tuning": a 64-token block size as an override of the
- * default);
- * num_q_heads a multiple of
- * num_kv_heads with G <= 16; dtypes (q, kv) = (F32, F32), (BF16, BF16) or
+ * default); num_q_heads a multiple of num_kv_heads with G <= 16; dtypes (q, kv) = (F32, F32), (BF16, BF16) or
  * (BF16, FP8_E4M3); out has q's dtype; q, out, k_cache, v_cache 16-byte
  * aligned.
  *
@@ -78,8 +76,9 @@
  * Errors.  A non-zero pa_status is returned before anything is enqueued when
  * the arguments are invalid.  A call with nothing to do (num_seqs == 0,
  * num_chunks == 0 or max_q_len == 0, num_tokens == 0) validates its sizes,
- * launches nothing and accepts NULL for its arrays.  PA_ERR_HIP reports a failed launch (including a
- * library built without a gfx950 code object).  There is no fallback path.
+ * launches nothing and accepts NULL for its arrays.  PA_ERR_HIP reports a
+ * failed launch (including a library built without a gfx950 code object).
+ * There is no fallback path.
  * Block-table contents are not checked: an entry outside [0, num_blocks) or
  * a seq_len above max_blocks_per_seq * block_size is undefined behaviour.
  */
@@ -151,7 +150,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * directly.  With at least 1024 (sequence, kv-head) pairs and at most 1024
  * sequences the workgroups take the sequences longest first (each
  * workgroup finds its sequence from seq_lens on the device), so the grid
- * does not end on a tail of long sequences; results are unchanged.  partition_size > 0 (a multiple of 16 tokens): split-KV; each
+ * does not end on a tail of long sequences; results are unchanged.
+ *
+ * partition_size > 0 (a multiple of 16 tokens): split-KV; each
  * partition p covers tokens [p*P, min((p+1)*P, L)) and writes its normalised
  * output and lse into `workspace`, then the log-sum-exp merge (the kernel of
  * pa_merge_partitions) writes out.  A sequence that fits in one partition
@@ -230,7 +231,8 @@ int pa_decode_noalloc(void* out, const void* q, int q_dtype,
  * Multi-query decode: each sequence has q_len queries, the newest q_len
  * tokens already in its cache, as when drafted tokens are verified in one
  * step (speculative decoding: in vllm-mblt 0.8.0, "Serve an EAGLE-3 Model",
- * the base model verifies each round's drafted tokens).  Query i of sequence b sits at position L - q_len + i
+ * the base model verifies each round's drafted tokens).  Query i of
+ * sequence b sits at position L - q_len + i
  * (L = seq_lens[b]) and attends to keys 0 .. L - q_len + i: the causal mask
  * of a prefill chunk whose context is L - q_len.
  *
