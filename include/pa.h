@@ -430,6 +430,26 @@ int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype,
                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 const float* k_scale, const float* v_scale, void* stream);
 
+/*
+ * A measurement aid, not a step of attention: reads the `bytes` bytes at buf
+ * once, front to back, and XORs the buffer's 32-bit words (little-endian)
+ * into the sink.  Timed over a buffer much larger than the device's caches it
+ * gives the measured HBM read rate beside which the attention kernels'
+ * live-K/V rates are reported.  nontemporal != 0 reads with the non-temporal
+ * loads the attention kernels use for K and V, 0 with plain loads.
+ * buf: device memory, 16-byte aligned, bytes a multiple of 16 (PA_ERR_ALIGN,
+ * PA_ERR_SHAPE).  sink: PA_STREAM_READ_SINK_WORDS device uint32 words,
+ * 4-byte aligned; each workgroup XORs its share into a word of its own, so
+ * the XOR of all the words changes by the buffer's XOR (zero the sink first
+ * to read the buffer's XOR off it).  Calls that overlap on one sink race.
+ * bytes == 0 launches nothing and accepts NULL for buf.  Enqueued on stream;
+ * the call does not wait.
+ */
+#define PA_STREAM_READ_SINK_WORDS 2048
+
+int pa_stream_read(const void* buf, size_t bytes, int nontemporal, uint32_t* sink,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@ ABI of ``include/pa.h``); this package is its thin Python binding:
 * :func:`merge_partitions`  log-sum-exp merge of partition results
 * :func:`prefill_chunk`     causal chunked prefill over a paged context
 * :func:`mixed_step`        decode rows and prefill chunks as one step
+* :func:`stream_read`       a plain read of one buffer (HBM read-rate probe)
 
 Importing the package loads ``libpa.so`` and fails if it is not built
 (``python paged_kv_cache_22_amd/build.py``).
@@ -17,9 +18,10 @@ from ._binding import (LIB_PATH, PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALA
                        decode_noalloc, STATIC_WORKSPACE_BYTES, decode_multi_query, decode_shared_prefix, decode_stages, PA_STAGE_ATTENTION, PA_STAGE_MERGE,
                        PA_STAGE_ALL,
                        decode_partitions, decode_workspace_size, lib, merge_partitions,
-                       mixed_step, prefill_chunk, status_string, write_kv)
+                       mixed_step, prefill_chunk, status_string, stream_read, STREAM_READ_SINK_WORDS,
+                       write_kv)
 
 __all__ = ["decode", "decode_noalloc", "STATIC_WORKSPACE_BYTES", "decode_multi_query", "decode_shared_prefix", "decode_stages", "PA_STAGE_ATTENTION", "PA_STAGE_MERGE",
-           "PA_STAGE_ALL", "decode_partitions", "merge_partitions", "mixed_step", "prefill_chunk", "write_kv",
+           "PA_STAGE_ALL", "decode_partitions", "merge_partitions", "mixed_step", "prefill_chunk", "stream_read", "STREAM_READ_SINK_WORDS", "write_kv",
            "decode_workspace_size", "status_string", "PAError", "lib", "LIB_PATH",
            "PA_F32", "PA_BF16", "PA_FP8_E4M3", "PA_PARTITION_BALANCED"]

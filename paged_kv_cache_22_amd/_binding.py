@@ -46,6 +46,7 @@ SIGNATURES = {
     "pa_mixed_step": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _vp, _sz,
                            _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _vp, _i,
                            _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
+    "pa_stream_read": (_i, [_vp, _sz, _i, _vp, _vp]),
 }
 
 
@@ -179,6 +180,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int,
 
 
 STATIC_WORKSPACE_BYTES = 64 << 20   # PA_STATIC_WORKSPACE_BYTES
+STREAM_READ_SINK_WORDS = 2048       # PA_STREAM_READ_SINK_WORDS
 
 
 def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len: int, out,
@@ -434,3 +436,22 @@ def write_kv(key, value, k_cache, v_cache, slot_mapping, *, k_scale=None, v_scal
                          NB, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream(key))
     _check("pa_write_kv", st)
     return k_cache, v_cache
+
+
+def stream_read(buf, *, nontemporal: bool = True, sink=None):
+    """Read a device buffer once (pa_stream_read): the measured HBM read rate
+    beside which the attention kernels' rates are reported.  Returns the sink,
+    STREAM_READ_SINK_WORDS int32 words whose XOR changes by the XOR of the
+    buffer's 32-bit words (a new zeroed sink when none is given)."""
+    torch = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor (libpa has no CPU path)")
+    if sink is None:
+        sink = torch.zeros(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    elif sink.numel() * sink.element_size() < 4 * STREAM_READ_SINK_WORDS:
+        raise ValueError(f"sink must hold {STREAM_READ_SINK_WORDS} 32-bit words")
+    st = lib.pa_stream_read(buf.data_ptr() if buf.numel() else None,
+                            buf.numel() * buf.element_size(), int(bool(nontemporal)),
+                            _dev(sink, "sink"), _stream(buf))
+    _check("pa_stream_read", st)
+    return sink

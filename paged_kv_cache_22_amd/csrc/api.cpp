@@ -692,6 +692,15 @@ int pa_mixed_step(void* dec_out, const void* dec_q, const int32_t* dec_block_tab
     return hip_status(pa::launch_prefill(a, stream));
 }
 
+int pa_stream_read(const void* buf, size_t bytes, int nontemporal, uint32_t* sink,
+                   void* stream) {
+    if (!sink || (bytes > 0 && !buf)) return PA_ERR_NULL;
+    if (bytes % 16) return PA_ERR_SHAPE;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return PA_ERR_ALIGN;
+    if (bytes == 0) return PA_OK;
+    return hip_status(pa::launch_stream_read(buf, bytes / 16, nontemporal ? 1 : 0, sink, stream));
+}
+
 int pa_write_kv(void* k_cache, void* v_cache, int kv_dtype, const void* key, const void* value,
                 int in_dtype, int key_stride, int value_stride, const int32_t* slot_mapping,
                 int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,

@@ -84,7 +84,7 @@ struct PrefillArgs {
     int part_stride;
     int max_blocks_per_seq;
     float scale;
-    // merge_rows > 0: before its own rows, the kernel merges rows 0 ..
+    // merge_rows > 0: after its own rows, the kernel merges rows 0 ..
     // merge_rows - 1 of a decode step's split-KV partials described by merge
     // (same head_dim and output dtype), one wave per row (a mixed step)
     int merge_rows;
@@ -129,5 +129,7 @@ int launch_prefill(const PrefillArgs& a, void* stream);
 // a prefill launch can run ahead of its own rows, bit for bit the same)
 bool merge_fusable(const MergeArgs& a);
 int launch_write_kv(const WriteArgs& a, void* stream);
+// XOR of n16 16-byte words at buf (folded to 32 bits) into *sink
+int launch_stream_read(const void* buf, size_t n16, int nontemporal, unsigned* sink, void* stream);
 
 }  // namespace pa

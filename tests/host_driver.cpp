@@ -78,6 +78,17 @@ int launch_write_kv(const WriteArgs&, void*) {
     ++g_launches;
     return 0;
 }
+
+int launch_stream_read(const void* buf, size_t n16, int, unsigned* sink, void*) {
+    ++g_launches;
+    // read every byte the kernel would read and every sink word it may write
+    const unsigned char* b = static_cast<const unsigned char*>(buf);
+    unsigned x = 0;
+    for (size_t i = 0; i < n16 * 16; ++i) x ^= (unsigned)b[i] << (8 * (i & 3));
+    for (int g = 1; g < PA_STREAM_READ_SINK_WORDS; ++g) sink[g] ^= 0u;
+    sink[0] ^= x;
+    return 0;
+}
 }  // namespace pa
 
 namespace {
@@ -220,6 +231,25 @@ int main() {
                                  need - 1, fake(5), nullptr, fake(6), ifake(7), 2048, 512, ifake(8),
                                  160, ifake(9), 4, PA_BF16, fake(10), fake(11), PA_BF16, 32, 8, 128,
                                  16, 100000, 0.088f, nullptr, nullptr, nullptr) == PA_ERR_WORKSPACE);
+    }
+
+    // the read probe hands the kernel exactly the buffer's 16-byte words
+    {
+        const size_t bytes = 4096 + 16;
+        Workspace buf(bytes), sink(PA_STREAM_READ_SINK_WORDS * sizeof(uint32_t));
+        unsigned char* b = static_cast<unsigned char*>(buf.p);
+        uint32_t want = 0;
+        for (size_t i = 0; i < bytes; ++i) {
+            b[i] = (unsigned char)(i * 131 + 7);
+            want ^= (uint32_t)b[i] << (8 * (i & 3));
+        }
+        uint32_t* x = static_cast<uint32_t*>(sink.p);
+        std::memset(x, 0, PA_STREAM_READ_SINK_WORDS * sizeof(uint32_t));
+        EXPECT(pa_stream_read(buf.p, bytes, 1, x, nullptr) == PA_OK);
+        uint32_t got = 0;
+        for (int g = 0; g < PA_STREAM_READ_SINK_WORDS; ++g) got ^= x[g];
+        EXPECT(got == want);
+        EXPECT(pa_stream_read(buf.p, bytes - 8, 1, x, nullptr) == PA_ERR_SHAPE);
     }
 
     // extreme sizes are refused, not overflowed

@@ -315,3 +315,20 @@ def test_mixed_step_empty_accepts_null_arrays():
     assert mixed_call(B=0, dout=None, dq=None, dbt=None, dsl=None, max_len=0, ws=None, wsb=0,
                       nc=0, mq=0, tq=0, pout=None, pq=None, cu=None, pbt=None, psl=None) == OK
     assert mixed_call(B=0, dout=None, dq=None, nc=0, mq=0, d=96) == UNSUP   # sizes still checked
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 4096, 1, P, None), NULL),         # no buffer
+    ((P, 4096, 1, None, None), NULL),         # no sink
+    ((P, 4104, 1, P, None), SHAPE),           # not whole 16-byte words
+    ((P + 8, 4096, 0, P, None), ALIGN),
+    ((P, 4096, 1, P + 2, None), ALIGN),
+    ((None, 0, 1, P, None), OK),              # nothing to read: nothing launched
+])
+def test_stream_read_rejects_before_launch(args, status):
+    assert pa.lib.pa_stream_read(*args) == status
+
+
+def test_stream_read_sink_size_matches_header():
+    m = re.search(r"#define PA_STREAM_READ_SINK_WORDS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == B.STREAM_READ_SINK_WORDS
