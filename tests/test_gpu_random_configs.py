@@ -20,8 +20,8 @@ from gpu_util import Dev, compare, f64
 
 pytestmark = pytest.mark.gpu
 
-N_DECODE = 24
-N_PREFILL = 12
+N_DECODE = 240
+N_PREFILL = 120
 
 
 def _common(rng):
@@ -120,8 +120,8 @@ def test_random_prefill(i):
     compare(f64(out), ref, c["kv"], what, out_rounding=True)
 
 
-N_WRITE = 12
-N_PREFIX = 12
+N_WRITE = 60
+N_PREFIX = 60
 
 
 def write_case(i):
@@ -224,3 +224,71 @@ def test_random_shared_prefix(i):
                                       wl.scale, wl.q_dtype, wl.kv_dtype, wl.k_scale, wl.v_scale)
         ref = ref.reshape(B, qn, Hq, d)
     compare(f64(out), ref, c["kv"], what, out_rounding=True)
+
+
+N_MIXED = 60
+
+
+def mixed_case(i):
+    rng = np.random.default_rng([i, 971])
+    c = _common(rng)
+    B = int(rng.integers(1, 13))
+    lens = rng.integers(1, int(rng.choice([40, 300, 1200])), size=B, endpoint=True)
+    lens[rng.random(B) < 0.15] = 0                       # idle sequences
+    lens[rng.integers(B)] = 1                            # the pool holds a block at least
+    P = int(rng.choice([-1, 0, 512, 16 * int(rng.integers(1, 9))]))
+    n = int(rng.integers(0, 5))                          # no chunks at all, now and then
+    q_lens = rng.integers(0, 80, size=n)
+    ctx = rng.integers(0, 300, size=n)
+    c.update(B=B, lens=lens.astype(np.int32), P=P, q_lens=q_lens.astype(np.int32),
+             ctx=ctx.astype(np.int32))
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_MIXED))
+def test_random_mixed_step(i):
+    """pa_mixed_step: bit for bit pa_decode followed by pa_prefill_chunk on
+    the same cache, and the oracle within the graded bar."""
+    import paged_kv_cache_22_amd as pa
+    from test_gpu_mixed_step import MixedDev, assert_same
+    c = mixed_case(i)
+    what = (f"mixed case {i}: {c['kv']} d={c['d']} bs={c['bs']} Hkv={c['hkv']} G={c['G']} "
+            f"B={c['B']} P={c['P']} lens={c['lens'].tolist()} q_lens={c['q_lens'].tolist()} "
+            f"ctx={c['ctx'].tolist()}")
+    hq = c["G"] * c["hkv"]
+    dec = W.decode_workload(seed=9000 + i, num_seqs=c["B"], num_q_heads=hq, num_kv_heads=c["hkv"],
+                            head_dim=c["d"], len_lo=0, len_hi=0, q_dtype=c["qd"],
+                            kv_dtype=c["kv"], block_size=c["bs"], seq_lens=c["lens"],
+                            name=f"random mixed decode {i}")
+    pre = W.prefill_workload(seed=9500 + i, q_lens=c["q_lens"], ctx_lens=c["ctx"],
+                             num_q_heads=hq, num_kv_heads=c["hkv"], head_dim=c["d"],
+                             q_dtype=c["qd"], kv_dtype=c["kv"], block_size=c["bs"],
+                             name=f"random mixed chunks {i}")
+    # the chunks' tables name blocks of the decode pool: one cache, one pair of scales
+    rng = np.random.default_rng([i, 972])
+    pre.block_table = rng.integers(0, dec.num_blocks, size=pre.block_table.shape).astype(np.int32)
+    pre.k_cache, pre.v_cache = dec.k_cache, dec.v_cache
+    pre.k_scale, pre.v_scale = dec.k_scale, dec.v_scale
+    m = MixedDev(dec, pre)
+    d = m.d
+    print(f"[random] {what}", flush=True)
+    sd = pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=dec.max_seq_len, scale=dec.scale,
+                   partition_size=c["P"], k_scale=d.ks, v_scale=d.vs)
+    sp, sl = pa.prefill_chunk(m.pq, m.cu, d.k, d.v, m.pbt, m.psl, max_q_len=pre.max_q_len,
+                              scale=pre.scale, k_scale=d.ks, v_scale=d.vs, want_lse=True)
+    md, mp, ml = pa.mixed_step(d.q, d.bt, d.sl, m.pq, m.cu, m.pbt, m.psl, d.k, d.v,
+                               max_seq_len=dec.max_seq_len, max_q_len=pre.max_q_len,
+                               partition_size=c["P"], scale=dec.scale, k_scale=d.ks, v_scale=d.vs,
+                               want_lse=True)
+    torch.cuda.synchronize()
+    assert_same(md, sd, what + " (decode rows)")
+    assert_same(mp, sp, what + " (chunk rows)")
+    assert_same(ml, sl, what + " (chunk lse)")
+    ref_d = oracle.decode(dec.q, dec.k_cache, dec.v_cache, dec.block_table, dec.seq_lens,
+                          dec.scale, dec.q_dtype, dec.kv_dtype, dec.k_scale, dec.v_scale)[0]
+    compare(f64(md), ref_d, c["kv"], what + " decode rows", out_rounding=True)
+    if pre.q.shape[0]:
+        ref_p, _ = oracle.prefill_chunk(pre.q, pre.cu_q_lens, pre.k_cache, pre.v_cache,
+                                        pre.block_table, pre.seq_lens, pre.scale, pre.q_dtype,
+                                        pre.kv_dtype, pre.k_scale, pre.v_scale)
+        compare(f64(mp), ref_p, c["kv"], what + " chunk rows", out_rounding=True)
