@@ -370,10 +370,11 @@ int pa_prefill_chunk(void* out, float* out_lse, const void* q, int q_dtype,
  * chunk part (pre_*, cu_q_lens, total_q, max_q_len, num_chunks: as there),
  * bit for bit; the shared arguments (dtypes, caches, head counts, head_dim,
  * block size, pool size, scale, fp8 scales) describe both.  When the decode
- * rows need a split-KV merge, it runs inside the chunks' launch, ahead of
- * each workgroup's own rows, instead of as a launch of its own: two launches
- * per step instead of three (a merge over 32 or more fixed partitions, which
- * takes a workgroup per row, keeps its own launch).  Every argument of both parts is validated
+ * rows need a split-KV merge, it runs inside the chunks' launch (the
+ * workgroups of the first half of the chunks' row tiles merge their share of
+ * the decode rows after their own rows) instead of as a launch of its own:
+ * two launches per step instead of three (a merge over 32 or more fixed
+ * partitions, which takes a workgroup per row, keeps its own launch).  Every argument of both parts is validated
  * before anything is enqueued; either part may be empty (num_seqs == 0, or
  * num_chunks == 0 / max_q_len == 0).  The workspace must not overlap any
  * output.

@@ -11,6 +11,10 @@ ABI of ``include/pa.h``); this package is its thin Python binding:
 * :func:`mixed_step`        decode rows and prefill chunks as one step
 * :func:`stream_read`       a plain read of one buffer (HBM read-rate probe)
 
+``paged_kv_cache_22_amd.checks`` holds opt-in host-side checks of the device
+arrays the C ABI does not validate (block-table entries, lengths, cu_q_lens,
+slot mappings), for tests and debugging.
+
 Importing the package loads ``libpa.so`` and fails if it is not built
 (``python paged_kv_cache_22_amd/build.py``).
 """
