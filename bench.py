@@ -616,6 +616,9 @@ def profile_one(args, W):
     if args.workload == "BLOCKS":
         print(json.dumps(time_block_sizes(torch, pa, W, args.steps, args.warmup, flush)), flush=True)
         return
+    if args.workload == "STREAM":
+        print(json.dumps(time_stream_read(torch, pa, flush, reps=args.steps)), flush=True)
+        return
     if args.workload == "WRITE":
         for wl in write_cases(W):
             print(json.dumps(time_write(torch, pa, wl, args.steps, args.warmup, flush)), flush=True)
@@ -648,10 +651,12 @@ def main():
                          "balanced split (equal work per resident workgroup), 0 = one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY", "BLOCKS", "PREFIX"],
+    ap.add_argument("--workload", default="C2", choices=["C2", "C3", "C4", "C5", "WRITE", "VERIFY", "BLOCKS", "PREFIX",
+                             "STREAM"],
                     help="time only this workload (default: the Llama-3-8B-shaped C2 headline "
                          "plus the others under per_config; WRITE = the cache writes, VERIFY = draft "
-                         "verification, BLOCKS = 32/64-token blocks, PREFIX = a shared-prefix batch)")
+                         "verification, BLOCKS = 32/64-token blocks, PREFIX = a shared-prefix batch, "
+                         "STREAM = the linear read rate of a 1 GiB buffer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (a known byte count "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
