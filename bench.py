@@ -261,12 +261,33 @@ def time_partition_kernel(torch, pa, d, wl, P, steps, warmup, flush):
     return [t.ms(i, 0, 1) for i in range(steps)]
 
 
+def checked(wl):
+    """Device copies of a workload, made after the host-side checks of what
+    the kernels read without validating it (every live block-table entry
+    inside the pool, lengths within their rows and the host-side bounds)."""
+    from paged_kv_cache_22_amd import checks
+    from workloads.device import Dev
+    if hasattr(wl, "cu_q_lens"):
+        checks.check_prefill_inputs(wl.cu_q_lens, wl.block_table, wl.seq_lens,
+                                    num_blocks=wl.num_blocks, block_size=wl.block_size,
+                                    max_q_len=wl.max_q_len, total_q=wl.total_q)
+    else:
+        checks.check_decode_inputs(wl.block_table, wl.seq_lens, num_blocks=wl.num_blocks,
+                                   block_size=wl.block_size, max_seq_len=wl.max_seq_len,
+                                   q_len=wl.q_len)
+    return Dev(wl)
+
+
 def mixed_devices(m):
     """Device copies of the mixed step: one KV cache shared by its decode rows
     and its chunks (they are one pool), with each part's own q, tables and
     lengths."""
+    from paged_kv_cache_22_amd import checks
     from workloads.device import Dev
-    dd = Dev(m.decode)
+    dd = checked(m.decode)
+    checks.check_prefill_inputs(m.prefill.cu_q_lens, m.prefill.block_table, m.prefill.seq_lens,
+                                num_blocks=m.decode.num_blocks, block_size=m.decode.block_size,
+                                max_q_len=m.prefill.max_q_len, total_q=m.prefill.total_q)
     dp = Dev.__new__(Dev)
     dp.wl = m.prefill
     dp.q = dev_like(m.prefill.q, m.prefill.q_dtype)
@@ -383,11 +404,10 @@ def time_verify(torch, pa, W, steps, warmup, flush, partition_size):
     512-4096 tokens, 4 queries each (pa_decode_multi_query, the 16 MFMA
     columns filled by 4 queries x 4 heads), against the same work done as 64
     prefill chunks of 4 rows (pa_prefill_chunk)."""
-    from workloads.device import Dev
     wl = W.decode_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
                            len_lo=512, len_hi=4096, q_dtype="bf16", kv_dtype="bf16", q_len=4,
                            pad=0, name="verify")
-    d = Dev(wl)
+    d = checked(wl)
     B, qn = wl.num_seqs, wl.q_len
     out = torch.empty_like(d.q)
     ws = torch.empty(max(pa.decode_workspace_size(B, qn * wl.num_q_heads, wl.head_dim,
@@ -432,13 +452,12 @@ def time_verify(torch, pa, W, steps, warmup, flush, partition_size):
 def time_block_sizes(torch, pa, W, steps, warmup, flush):
     """The headline batch (C2's lengths, heads and data recipe) paged with
     32- and 64-token blocks, balanced split-KV."""
-    from workloads.device import Dev
     res = {}
     for bs in (32, 64):
         w = W.decode_workload(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
                               len_lo=512, len_hi=4096, q_dtype="bf16", kv_dtype="bf16",
                               block_size=bs, pad=0, name=f"C2 bs={bs}")
-        d = Dev(w)
+        d = checked(w)
         s, _ = time_decode(torch, pa, d, w, -1, steps, warmup, flush)
         ms = sum(s) / len(s)
         res[str(bs)] = {"ms_per_step": round(ms, 5), "kv_GBps": round(w.kv_bytes() / ms / 1e6, 2),
@@ -602,7 +621,6 @@ def profile_one(args, W):
     """Time one non-headline workload alone (for per-kernel profiling)."""
     import torch
     import paged_kv_cache_22_amd as pa
-    from workloads.device import Dev
     flush = CacheFlush(torch)
     if args.workload == "VERIFY":
         print(json.dumps(time_verify(torch, pa, W, args.steps, args.warmup, flush,
@@ -635,7 +653,7 @@ def profile_one(args, W):
         res.update(mixed_summary(m, args.partition_size, one, step, dec, pre))
     else:
         w = W.config3(pad=0) if n == 3 else W.config5(pad=0, partition_size=args.partition_size)
-        dd = Dev(w)
+        dd = checked(w)
         s, k = time_decode(torch, pa, dd, w, w.partition_size, args.steps, args.warmup, flush)
         res.update(decode_summary(w, s, k))
     print(json.dumps(res), flush=True)
@@ -678,11 +696,10 @@ def main():
 
     import torch
     import paged_kv_cache_22_amd as pa
-    from workloads.device import Dev
 
     torch.cuda.init()
     flush = CacheFlush(torch)
-    d = Dev(wl)
+    d = checked(wl)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     step_ms, _ = time_decode(torch, pa, d, wl, args.partition_size, args.steps,
@@ -702,7 +719,7 @@ def main():
         # sequences of 256-2048 tokens, no merge), each also balanced
         for n, P in ((3, 512), (5, 0)):
             w = W.build_config(n, pad=0) if n == 3 else W.build_config(n, pad=0, partition_size=P)
-            dd = Dev(w)
+            dd = checked(w)
             s, k = time_decode(torch, pa, dd, w, P, 20, 3, flush)
             per_config[w.name] = decode_summary(w, s, k)
             per_config[w.name]["workload"] = W.CONFIG_NAMES[n]
