@@ -126,7 +126,7 @@ int launch_decode(const DecodeArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
 // whether launch_merge would merge a's rows with one wave per row (the form
-// a prefill launch can run ahead of its own rows, bit for bit the same)
+// a prefill launch can run after its own rows, bit for bit the same)
 bool merge_fusable(const MergeArgs& a);
 int launch_write_kv(const WriteArgs& a, void* stream);
 // XOR of n16 16-byte words at buf (folded to 32 bits) into *sink
