@@ -33,6 +33,28 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# Per-file departures from HIP_FLAGS.  The multi-query decode kernels keep
+# their MFMA accumulators in AGPRs: in the VGPR form their results varied
+# from call to call on identical inputs (measured on MI355X), in the AGPR
+# form they repeat bit for bit at the same speed.
+FILE_FLAGS_DROP = {
+    "decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def flags_for(name: str) -> list:
+    """HIP_FLAGS for one csrc file, with its departures applied."""
+    flags = list(HIP_FLAGS)
+    drop = FILE_FLAGS_DROP.get(name, [])
+    if drop:
+        for i in range(len(flags) - len(drop) + 1):
+            if flags[i:i + len(drop)] == drop:
+                del flags[i:i + len(drop)]
+                break
+        else:
+            raise RuntimeError(f"{name}: flags {drop} not in HIP_FLAGS")
+    return flags
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -58,7 +80,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     objs = []
     for f in srcs:
         obj = os.path.join(BUILD, f + ".o")
-        jobs.append([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, f), "-o", obj])
+        jobs.append([hipcc, *flags_for(f), *extra_flags, "-c", os.path.join(CSRC, f), "-o", obj])
         objs.append(obj)
     api_obj = os.path.join(BUILD, "api.cpp.o")
     host_defs = [f for f in extra_flags if f.startswith("-D")]

@@ -123,6 +123,9 @@ int static_workspace(void** ptr, size_t* bytes);
 
 // Each returns 0 on success or the hipError_t of a failed launch.
 int launch_decode(const DecodeArgs& a, void* stream);
+// the same for a.q_len > 1 (called by launch_decode / balanced_splits)
+int launch_decode_mq(const DecodeArgs& a, void* stream);
+int balanced_splits_mq(const DecodeArgs& a);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
 // whether launch_merge would merge a's rows with one wave per row (the form

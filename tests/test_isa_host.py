@@ -35,7 +35,8 @@ def device_asm(tmp_path_factory):
 
     def one(src):
         dst = os.path.join(out, os.path.basename(src) + ".s")
-        p = subprocess.run([hipcc, *B.HIP_FLAGS, "--cuda-device-only", "-S", src, "-o", dst],
+        p = subprocess.run([hipcc, *B.flags_for(os.path.basename(src)), "--cuda-device-only", "-S",
+                            src, "-o", dst],
                            capture_output=True, text=True)
         assert p.returncode == 0, p.stderr[-2000:]
         return os.path.basename(src), open(dst).read()
@@ -55,8 +56,8 @@ def test_no_scratch_spills(device_asm):
     for name, text in device_asm.items():
         sizes = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
         with open(os.path.join(CSRC, name)) as f:
-            has_kernels = "__global__" in f.read()
-        assert bool(sizes) == has_kernels, f"{name}: kernel descriptors {len(sizes)}"
+            has_kernels = "__global__" in f.read()   # (or from the headers it includes)
+        assert sizes or not has_kernels, f"{name}: no kernel descriptors"
         assert all(int(x) == 0 for x in sizes), f"{name}: a kernel uses scratch ({sizes})"
 
 
