@@ -88,3 +88,43 @@ def test_prefill_mixed_and_shared_prefix_repeat():
     print("[determinism] shared prefix", flush=True)
     assert_repeats("shared prefix", lambda: pa.decode_shared_prefix(
         *args, max_seq_len=int(sp.suffix_lens.max()), partition_size=512, scale=wl.scale))
+
+
+SHAPES = [
+    # (head_dim, q-heads, kv-heads, block size, KV dtype, queries per sequence)
+    (64, 40, 10, 16, "bf16", 1), (64, 40, 10, 32, "fp8", 1), (128, 32, 32, 16, "bf16", 1),
+    (128, 64, 4, 64, "bf16", 1), (128, 32, 8, 32, "f32", 1), (64, 16, 2, 16, "bf16", 2),
+    (128, 16, 16, 64, "bf16", 4), (64, 32, 8, 16, "f32", 2),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"d{s[0]}-{s[1]}x{s[2]}-bs{s[3]}-{s[4]}-q{s[5]}"
+                                                for s in SHAPES])
+def test_other_shapes_repeat(shape):
+    """Head dims, group sizes 1-16, block sizes 16/32/64 and dtypes beyond the
+    Llama-3-8B layer, in the three split modes, and the same caches as
+    prefill chunks."""
+    import paged_kv_cache_22_amd as pa
+    d_, hq, hkv, bs, kv, ql = shape
+    qd = "f32" if kv == "f32" else "bf16"
+    wl = W.decode_workload(seed=11, num_seqs=24, num_q_heads=hq, num_kv_heads=hkv, head_dim=d_,
+                           len_lo=300, len_hi=3000, q_dtype=qd, kv_dtype=kv, block_size=bs,
+                           q_len=ql if ql > 1 else 0, pad=0)
+    d = Dev(wl)
+    for P in (-1, 0, 256):
+        print(f"[determinism] {shape} P={P}", flush=True)
+        if ql > 1:
+            fn = lambda: pa.decode_multi_query(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                                               scale=wl.scale, partition_size=P, k_scale=d.ks,
+                                               v_scale=d.vs)
+        else:
+            fn = lambda: pa.decode(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                                   scale=wl.scale, partition_size=P, k_scale=d.ks, v_scale=d.vs)
+        assert_repeats(f"{shape} P={P}", fn)
+    pw = W.prefill_workload(seed=12, q_lens=[200, 37, 128], ctx_lens=[900, 15, 2000],
+                            num_q_heads=hq, num_kv_heads=hkv, head_dim=d_, q_dtype=qd, kv_dtype=kv,
+                            block_size=bs)
+    p = Dev(pw)
+    assert_repeats(f"{shape} prefill", lambda: pa.prefill_chunk(
+        p.q, p.cu, p.k, p.v, p.bt, p.sl, max_q_len=pw.max_q_len, scale=pw.scale, k_scale=p.ks,
+        v_scale=p.vs, want_lse=True))
