@@ -10,7 +10,8 @@
 // with AGPR accumulators (and, for the balanced kernel, without the
 // three-waves-per-SIMD hint that forces the VGPR form) every call repeats
 // bit for bit, at the same speed (draft verification, 64 x 4 queries:
-// balanced 116.5 against 118.1 us, one pass 118.8 against 118.4).
+// balanced 116.5 against 118.1 us, one pass 118.8 against 118.4), and the
+// balanced kernel then has room to stage its partials in LDS (112.8 us).
 #include "decode_kernels.h"
 
 namespace pa {
