@@ -69,7 +69,10 @@
  * workgroups of the balanced decode mode the device holds at once (one
  * occupancy query on the first balanced call) and the address of
  * pa_decode_noalloc's fixed buffer (looked up on its first call).  Make
- * those first calls outside graph capture.  Table entries at or past
+ * those first calls outside graph capture.  Results are reproducible: the
+ * same arguments and device data give the same output bits on the same
+ * device, call after call (every floating-point sum has a fixed order; the
+ * only atomics are integer counts in LDS).  Table entries at or past
  * ceil(seq_len / block_size) and cache slots past seq_len are never read
  * (they may hold anything, NaN included).
  *
