@@ -377,6 +377,31 @@ def test_chunking_equals_one_pass():
     assert np.abs(dec[0] - whole[L - 1]).max() < 1e-12
 
 
+def test_verify_queries_equal_truncated_decodes():
+    """Draft verification: the newest q_len cached tokens of a sequence of L
+    tokens as queries.  Query i sits at position L - q_len + i, so it is an
+    ordinary decode step over the first L - q_len + 1 + i tokens; the
+    oracle's reference for it (one prefill chunk of q_len rows per
+    sequence) must equal those decode steps exactly, for every query."""
+    rng = np.random.default_rng(21)
+    q_len, Hkv, G, d = 4, 2, 4, 16
+    lens = [37, 64, 5, 4]
+    Ks = [rng.standard_normal((L, Hkv, d)) for L in lens]
+    Vs = [rng.standard_normal((L, Hkv, d)) for L in lens]
+    kp, vp, table, sl = scatter_to_pages(Ks, Vs, 16, rng)
+    kp, vp = f32(kp), f32(vp)
+    B = len(lens)
+    q = f32(rng.standard_normal((B * q_len, Hkv * G, d)))
+    cu = np.arange(0, B * q_len + 1, q_len, dtype=np.int32)
+    ref, _ = oracle.prefill_chunk(q, cu, kp, vp, table, sl, 0.3, "f32", "f32")
+    for b, L in enumerate(lens):
+        for i in range(q_len):
+            row = b * q_len + i
+            dec, _ = oracle.decode(q[row:row + 1], kp, vp, table[b:b + 1],
+                                   np.array([L - q_len + 1 + i], np.int32), 0.3, "f32", "f32")
+            assert np.abs(dec[0] - ref[row]).max() < 1e-12, (b, i)
+
+
 def test_prefix_sharing_equals_private_copies():
     wl = W.config4()
     pre = wl.prefill
@@ -460,6 +485,7 @@ def _pins_pass():
         test_uniform_scores_give_mean_of_v(17)
         test_equal_keys_at_huge_logits_give_mean_of_v()
         test_worked_example_two_tokens()
+        test_verify_queries_equal_truncated_decodes()
     except Exception:          # a wrong shape counts as a caught mistake too
         return False
     return True
@@ -599,3 +625,26 @@ def test_mutation_round_to_truncates(monkeypatch):
     monkeypatch.setattr(A, "round_to", trunc)
     with pytest.raises(AssertionError):
         test_round_to_bf16_matches_torch_cast()
+
+
+def test_mutation_verify_queries_see_the_whole_sequence(monkeypatch):
+    """A chunk's queries all attending to every cached token (the causal
+    limit inside the chunk forgotten) must fail a pin."""
+    orig = A.attend
+
+    def prefill_bad(q, cu, kc, vc, bt, sl, scale, qd, kd, k_scale=None, v_scale=None, items=None):
+        total_q, Hq, d = q.shape
+        G = Hq // kc.shape[1]
+        qf = A.widen(q, qd)
+        out = np.zeros((total_q, Hq, d)); lse = np.zeros((total_q, Hq))
+        for c in range(len(sl)):
+            q0, q1 = int(cu[c]), int(cu[c + 1]); L = int(sl[c])
+            for h in range(kc.shape[1]):
+                K, V = A.gather_kv(kc, vc, bt[c], L, h, kd)
+                for i in range(q1 - q0):
+                    for g in range(G):
+                        out[q0 + i, h * G + g], lse[q0 + i, h * G + g] = orig(
+                            qf[q0 + i, h * G + g], K, V, scale)
+        return out, lse
+    monkeypatch.setattr(oracle, "prefill_chunk", prefill_bad)
+    assert not _pins_pass()
