@@ -136,3 +136,44 @@ def test_spec_verify_llama3_8b_shape_full():
                            name="verify C2 shape")
     ref = oracle_mq(wl)
     compare(f64(run_mq(Dev(wl), 1024)), ref, "bf16", "spec verify 64 x 4 queries")
+
+
+def test_multi_query_in_a_captured_graph():
+    """pa_decode_multi_query (balanced and 512-token partitions) captured
+    once in a HIP graph and replayed with new queries: every replay equals
+    the eager calls bit for bit (the kernels stage their partials in LDS and
+    keep no state between calls beyond the workspace they fill)."""
+    import paged_kv_cache_22_amd as pa
+    wl = W.decode_workload(seed=431, num_seqs=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           len_lo=600, len_hi=3000, q_dtype="bf16", kv_dtype="bf16", q_len=4, pad=0)
+    d = Dev(wl)
+    modes = (-1, 512)
+    B, qn, Hq, D = wl.q.shape
+    ws = {P: torch.empty(max(pa.decode_workspace_size(B, qn * Hq, D, wl.max_seq_len, P), 256),
+                         dtype=torch.uint8, device="cuda") for P in modes}
+    outs = {P: torch.empty_like(d.q) for P in modes}
+
+    def step():
+        for P in modes:
+            pa.decode_multi_query(d.q, d.k, d.v, d.bt, d.sl, max_seq_len=wl.max_seq_len,
+                                  scale=wl.scale, partition_size=P, out=outs[P], workspace=ws[P])
+
+    step()                       # eager warm-up: the occupancy query runs outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(432)
+    for rep in range(3):
+        d.q.copy_(torch.from_numpy(W.to_bf16_bits(
+            rng.standard_normal(wl.q.shape).astype(np.float32)).view(np.int16)).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        print(f"[graph] multi-query replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        got = {P: outs[P].clone() for P in modes}
+        step()
+        torch.cuda.synchronize()
+        for P in modes:
+            assert torch.equal(got[P].view(torch.int16), outs[P].view(torch.int16)), (rep, P)
