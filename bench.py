@@ -38,7 +38,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_PROFILE = os.path.join(PROFILES, "decode_kernel_bf16_llama3_8b_c2_traffic.txt")
-KERNEL_SOURCES = ["decode.hip", "tiles.h", "device.h"]
+KERNEL_SOURCES = ["decode_kernels.h", "decode.hip", "tiles.h", "device.h"]
 
 
 def kernel_source_hash():
